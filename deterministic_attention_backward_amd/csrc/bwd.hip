@@ -1,0 +1,586 @@
+// Attention backward kernels for gfx950: pre-pass, main tile kernel with the
+// ordered dQ reduction, and the dQ conversion pass of the atomic variant.
+//
+// Gradient (per head, scale c, from the given O and LSE):
+//   P = exp(c Q K^T - LSE)   dV = P^T dO   dP = dO V^T   Delta = rowsum(dO * O)
+//   dS = P * (dP - Delta)    dQ = c dS K   dK = c dS^T Q
+//
+// Work decomposition (DASH, Dutch and Japanese technical summaries §2.1: all
+// work of one KV tile stays on one processor so that its accumulators stay in
+// registers): a persistent grid of workgroups takes "units" from a ticket
+// counter; a unit is one worker of one head (one KV tile, two for Symmetric
+// Shift). The unit walks its tasks (query tile i, KV tile j) in the order the
+// schedule fixes, accumulates dK_j/dV_j in MFMA accumulators and, per query
+// sub-tile, hands its dQ partial to the fp32 dQ workspace in the schedule's
+// order: wait until the sub-tile's counter equals r(i, j), add, publish,
+// increment. The last contributor converts to bf16 and writes dq directly.
+#include "common.hpp"
+#include "launch.hpp"
+#include "schedule.hpp"
+
+namespace attn {
+
+// --------------------------------------------------------------------------------------
+// pre-pass: Delta = rowsum(dO * O) in fp32, LSE in base 2, counters and ticket reset.
+
+struct PreParams {
+  const bf16 *o, *dout;
+  const float* lse;
+  float *lse2, *delta, *dq_ws;
+  int *counters, *header;
+  long long rows;       // BH * S_pad
+  int S, S_pad;
+  long long n_counters;
+  long long dq_ws_elems;  // > 0: zero the dQ accumulator (atomic variant)
+  int poison;
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
+  const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long nthreads = (long long)gridDim.x * blockDim.x;
+  const int sub = threadIdx.x % LPR;
+  for (long long base = gtid / LPR; base < p.rows; base += nthreads / LPR) {
+    const long long bh = base / p.S_pad;
+    const int s = (int)(base % p.S_pad);
+    float acc = 0.0f;
+    if (s < p.S) {
+      const long long off = (bh * p.S + s) * D + sub * 8;
+      const bf16x8 ov = *(const bf16x8*)(p.o + off);
+      const bf16x8 dv = *(const bf16x8*)(p.dout + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)dv[e];
+    }
+    // fixed butterfly over the LPR lanes of this row: the same order every run
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, LPR);
+    if (sub == 0) {
+      p.delta[base] = (s < p.S) ? acc : 0.0f;
+      p.lse2[base] = (s < p.S) ? p.lse[bh * p.S + s] * 1.4426950408889634f : __builtin_inff();
+    }
+  }
+  // every counter starts at 0; the optional poison value (an unreachable turn,
+  // used to exercise the wait bound) is written by the thread that owns that slot
+  for (long long i = gtid; i < p.n_counters; i += nthreads)
+    p.counters[i] = (p.poison && i == p.n_counters - 1) ? 0x40000000 : 0;
+  if (gtid < 64) p.header[gtid] = 0;
+  for (long long i = gtid * 4; i < p.dq_ws_elems; i += nthreads * 4)
+    *(f32x4*)(p.dq_ws + i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// --------------------------------------------------------------------------------------
+// main kernel
+
+struct MainParams {
+  const bf16 *q, *k, *v;
+  const bf16* dout;
+  bf16 *dq, *dk, *dv;
+  const float *lse2, *delta;
+  float *dq_ws, *park;
+  int *counters, *header;
+  int S, S_pad, N, n_qsub, n_workers, n_units, sched;
+  float scale, scale_log2;
+  uint32_t wait_limit;
+};
+
+template <int D, int T, int BR, bool CAUSAL, bool ATOMIC>
+__global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) {
+  constexpr int NW = T / 32;       // waves; wave w owns keys 32w..32w+31 of the KV tile
+  constexpr int NT = NW * 64;
+  constexpr int DP = D + 8;        // padded LDS row lengths (bf16 elements)
+  constexpr int BRP = BR + 8;
+  constexpr int TP = T + 8;
+  constexpr int KC = D / 16;       // 16-wide k-chunks over the feature dimension
+  constexpr int ND = D / 32;       // 32-wide feature blocks
+  constexpr int MB = BR / 32;      // 32-row query blocks per sub-tile
+  constexpr int NSUB = T / BR;     // query sub-tiles per task
+  constexpr int QB = MB * ND;      // 32x32 blocks of a dQ sub-tile
+  constexpr int QBW = QB / NW;     // ... per wave
+  constexpr int GROUPS = (BR / 4) * (D / 8);  // staging pieces: 4 rows x 8 features
+  constexpr int GPT = GROUPS / NT;
+  static_assert(QB % NW == 0 && GROUPS % NT == 0 && T % BR == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) bf16 sQ[BR * DP];    // Q sub-tile [row][d]
+  __shared__ __attribute__((aligned(16))) bf16 sQT[D * BRP];   // Q sub-tile [d][row]
+  __shared__ __attribute__((aligned(16))) bf16 sO[BR * DP];    // dO sub-tile [row][d]
+  __shared__ __attribute__((aligned(16))) bf16 sOT[D * BRP];   // dO sub-tile [d][row]
+  __shared__ __attribute__((aligned(16))) bf16 sKT[D * TP];    // K tile [d][key]
+  __shared__ __attribute__((aligned(16))) bf16 sdS[BR * TP];   // dS sub-tile [row][key]
+  __shared__ __attribute__((aligned(16))) float sL[BR];        // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sDl[BR];       // Delta
+  __shared__ int sUnit;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int S = p.S;
+
+  bf16x8 Kr[KC], Vr[KC];           // this wave's 32 keys as MFMA B operands
+  f32x16 dKa[ND], dVa[ND];         // dK, dV accumulators of the current KV tile
+  u32x4 stq[GPT][4], sto[GPT][4];  // staged next sub-tile
+  float stl = 0.0f, std_ = 0.0f;
+
+  auto stage_load = [&](int bh, int qrow0) {
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int gi = tid + g * NT;
+      const int qg = gi / (D / 8), dg = gi % (D / 8);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = qrow0 + qg * 4 + rr;
+        if (row < S) {
+          const size_t off = ((size_t)bh * S + row) * D + dg * 8;
+          stq[g][rr] = *(const u32x4*)(p.q + off);
+          sto[g][rr] = *(const u32x4*)(p.dout + off);
+        } else {
+          stq[g][rr] = u32x4{0u, 0u, 0u, 0u};
+          sto[g][rr] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    if (tid < BR) {
+      const size_t off = (size_t)bh * p.S_pad + qrow0 + tid;
+      stl = p.lse2[off];
+      std_ = p.delta[off];
+    }
+  };
+
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int gi = tid + g * NT;
+      const int qg = gi / (D / 8), dg = gi % (D / 8);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        *(u32x4*)&sQ[(qg * 4 + rr) * DP + dg * 8] = stq[g][rr];
+        *(u32x4*)&sO[(qg * 4 + rr) * DP + dg * 8] = sto[g][rr];
+      }
+      bf16x8 qv[4], ov[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        qv[rr] = __builtin_bit_cast(bf16x8, stq[g][rr]);
+        ov[rr] = __builtin_bit_cast(bf16x8, sto[g][rr]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x4 tq, to;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          tq[rr] = qv[rr][e];
+          to[rr] = ov[rr][e];
+        }
+        *(bf16x4*)&sQT[(dg * 8 + e) * BRP + qg * 4] = tq;
+        *(bf16x4*)&sOT[(dg * 8 + e) * BRP + qg * 4] = to;
+      }
+    }
+    if (tid < BR) {
+      sL[tid] = stl;
+      sDl[tid] = std_;
+    }
+  };
+
+  auto load_kv = [&](int bh, int kv) {
+    const int key = kv * T + 32 * w + l32;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (key < S) {
+        const size_t off = ((size_t)bh * S + key) * D + 16 * c + 8 * hh;
+        Kr[c] = *(const bf16x8*)(p.k + off);
+        Vr[c] = *(const bf16x8*)(p.v + off);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          Kr[c][e] = (bf16)0.0f;
+          Vr[c][e] = (bf16)0.0f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sKT[(16 * c + 8 * hh + e) * TP + 32 * w + l32] = Kr[c][e];
+    }
+  };
+
+  auto finalize_kv = [&](int bh, int kv) {
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv * T + 32 * w + 8 * (i / 4) + 4 * hh + (i % 4);
+        if (key < S) {
+          const size_t off = ((size_t)bh * S + key) * D + 32 * n + l32;
+          p.dk[off] = to_bf16(dKa[n][i] * p.scale);
+          p.dv[off] = to_bf16(dVa[n][i]);
+        }
+      }
+    }
+  };
+
+  // Symmetric Shift parking: one slot per (workgroup, tile of the pair).
+  auto park_acc = [&](int slot, bool load) {
+    float* base = p.park + ((size_t)blockIdx.x * 2 + slot) * (size_t)(2 * ND * 16 * NT);
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float* a = base + (size_t)((n * 16 + i) * NT + tid);
+        float* b = base + (size_t)(((ND + n) * 16 + i) * NT + tid);
+        if (load) {
+          dKa[n][i] = *a;
+          dVa[n][i] = *b;
+        } else {
+          *a = dKa[n][i];
+          *b = dVa[n][i];
+        }
+      }
+    }
+    wait_vmem();
+  };
+
+  for (;;) {
+    __syncthreads();
+    if (tid == 0) sUnit = atomicAdd(&p.header[0], 1);
+    __syncthreads();
+    const int unit = sUnit;
+    if (unit >= p.n_units) break;
+    const int bh = unit / p.n_workers;
+    const int wk = unit % p.n_workers;
+    const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
+    const int total = ntasks * NSUB;
+
+    // the (at most two) KV tiles this unit owns and the last task of each
+    int tileA = -1, tileB = -1, lastA = -1, lastB = -1;
+    for (int t = 0; t < ntasks; ++t) {
+      const int kv = sched_task(p.N, CAUSAL, p.sched, wk, t).kv;
+      if (tileA < 0 || kv == tileA) {
+        tileA = kv;
+        lastA = t;
+      } else {
+        tileB = kv;
+        lastB = t;
+      }
+    }
+    int cur_kv = -1;
+    bool parkedA = false, parkedB = false;
+
+    {
+      const Task t0 = sched_task(p.N, CAUSAL, p.sched, wk, 0);
+      stage_load(bh, t0.q * T);
+      stage_store();
+      if (total > 1) {
+        const Task t1 = sched_task(p.N, CAUSAL, p.sched, wk, 1 / NSUB);
+        stage_load(bh, t1.q * T + (1 % NSUB) * BR);
+      }
+    }
+
+    for (int idx = 0; idx < total; ++idx) {
+      const int t = idx / NSUB;
+      const int sidx = idx % NSUB;
+      const Task task = sched_task(p.N, CAUSAL, p.sched, wk, t);
+      const int qi = task.q, kj = task.kv;
+
+      if (kj != cur_kv) {
+        if (cur_kv >= 0) {
+          const bool isA = (cur_kv == tileA);
+          const int last = isA ? lastA : lastB;
+          if (t <= last) {
+            park_acc(isA ? 0 : 1, false);
+            if (isA) parkedA = true; else parkedB = true;
+          } else {
+            finalize_kv(bh, cur_kv);
+          }
+        }
+        __syncthreads();  // every wave is done reading sKT
+        load_kv(bh, kj);
+        const bool isA = (kj == tileA);
+        if (isA ? parkedA : parkedB) {
+          park_acc(isA ? 0 : 1, true);
+          if (isA) parkedA = false; else parkedB = false;
+        } else {
+#pragma unroll
+          for (int n = 0; n < ND; ++n) {
+            dKa[n] = zero16();
+            dVa[n] = zero16();
+          }
+        }
+        cur_kv = kj;
+      }
+
+      const int q_base = qi * T + sidx * BR;   // first query row of this sub-tile
+      const int kv_base = kj * T;
+      __syncthreads();  // staged sub-tile and sKT visible
+
+      // ---- S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q
+      const int key_g = kv_base + 32 * w + l32;
+      const bool key_ok = key_g < S;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const bf16x8 qa = *(const bf16x8*)&sQ[(32 * m + l32) * DP + 16 * c + 8 * hh];
+          const bf16x8 oa = *(const bf16x8*)&sO[(32 * m + l32) * DP + 16 * c + 8 * hh];
+          s = mfma32(qa, Kr[c], s);
+          dp = mfma32(oa, Vr[c], dp);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
+          const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int i = 4 * a + b;
+            const int q_g = q_base + 32 * m + 8 * a + 4 * hh + b;
+            float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+            const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
+            pv = vis ? pv : 0.0f;
+            s[i] = pv;
+            dp[i] = pv * (dp[i] - D4[b]);
+          }
+        }
+        const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
+        const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+          const bf16* ro = &sOT[(32 * n + l32) * BRP + 32 * m + 4 * hh];
+          const bf16* rq = &sQT[(32 * n + l32) * BRP + 32 * m + 4 * hh];
+          const bf16x8 ob0 = cat44(*(const bf16x4*)ro, *(const bf16x4*)(ro + 8));
+          const bf16x8 ob1 = cat44(*(const bf16x4*)(ro + 16), *(const bf16x4*)(ro + 24));
+          const bf16x8 qb0 = cat44(*(const bf16x4*)rq, *(const bf16x4*)(rq + 8));
+          const bf16x8 qb1 = cat44(*(const bf16x4*)(rq + 16), *(const bf16x4*)(rq + 24));
+          dVa[n] = mfma32(pb0, ob0, dVa[n]);
+          dVa[n] = mfma32(pb1, ob1, dVa[n]);
+          dKa[n] = mfma32(db0, qb0, dKa[n]);
+          dKa[n] = mfma32(db1, qb1, dKa[n]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * m + 8 * (i / 4) + 4 * hh + (i % 4);
+          sdS[row * TP + 32 * w + l32] = (i < 8) ? db0[i] : db1[i - 8];
+        }
+      }
+      __syncthreads();  // sdS complete; staged Q/dO no longer read
+
+      if (idx + 1 < total) {
+        stage_store();
+        if (idx + 2 < total) {
+          const int t2 = (idx + 2) / NSUB;
+          const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, t2);
+          stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
+        }
+      }
+
+      // ---- dQ partial = dS K for this wave's 32x32 blocks of the sub-tile
+      f32x16 dqa[QBW];
+#pragma unroll
+      for (int bi = 0; bi < QBW; ++bi) {
+        const int b = w + bi * NW;
+        const int mb = b / ND, nb = b % ND;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int c = 0; c < T / 16; ++c) {
+          const bf16x8 a = *(const bf16x8*)&sdS[(32 * mb + l32) * TP + 16 * c + 8 * hh];
+          const bf16x8 kb = *(const bf16x8*)&sKT[(32 * nb + l32) * TP + 16 * c + 8 * hh];
+          acc = mfma32(a, kb, acc);
+        }
+        dqa[bi] = acc;
+      }
+
+      // ---- hand the partial to dQ tile qi, sub-tile sidx
+      float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;
+      if (ATOMIC) {
+#pragma unroll
+        for (int bi = 0; bi < QBW; ++bi) {
+          const int b = w + bi * NW;
+          const int mb = b / ND, nb = b % ND;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 32 * mb + 8 * (i / 4) + 4 * hh + (i % 4);
+            unsafeAtomicAdd(wsrow + (size_t)row * D + 32 * nb + l32, dqa[bi][i]);
+          }
+        }
+      } else {
+        const int cidx = bh * p.n_qsub + qi * NSUB + sidx;
+        const int r = sched_rank(p.N, CAUSAL, p.sched, qi, kj);
+        const bool last = (r == sched_contributors(p.N, CAUSAL, qi) - 1);
+        if (r > 0) {
+          if (tid == 0) {
+            uint32_t it = 0;
+            while (__hip_atomic_load(&p.counters[cidx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != r) {
+              if (++it >= p.wait_limit) {
+                __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int bi = 0; bi < QBW; ++bi) {
+          const int b = w + bi * NW;
+          const int mb = b / ND, nb = b % ND;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = 32 * mb + 8 * (i / 4) + 4 * hh + (i % 4);
+            float* a = wsrow + (size_t)row * D + 32 * nb + l32;
+            float val = dqa[bi][i];
+            if (r > 0) val = *a + val;
+            if (last) {
+              if (q_base + row < S)
+                p.dq[((size_t)bh * S + q_base + row) * D + 32 * nb + l32] = to_bf16(val * p.scale);
+            } else {
+              *a = val;
+            }
+          }
+        }
+        if (!last) {
+          wait_vmem();      // this wave's dQ stores have completed
+          __syncthreads();  // ... and so have every other wave's
+          if (tid == 0)  // next turn; an increment keeps a poisoned counter out of reach
+            __hip_atomic_fetch_add(&p.counters[cidx], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (cur_kv >= 0) finalize_kv(bh, cur_kv);
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// post-pass (atomic variant): dq = bf16(scale * dQ accumulator)
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, long long BH, int S,
+                                                       int S_pad, float scale) {
+  const long long n4 = BH * S * (D / 4);
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long e = i * 4;
+    const long long row = e / D;  // bh * S + s
+    const int col = (int)(e % D);
+    const long long bh = row / S;
+    const int s = (int)(row % S);
+    const f32x4 v = *(const f32x4*)(dq_ws + ((bh * S_pad + s) * D + col));
+    bf16x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = to_bf16(v[j] * scale);
+    *(bf16x4*)(dq + e) = o;
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// launcher
+
+template <int D, int T, int BR, bool CAUSAL, bool ATOMIC>
+static hipError_t launch_main(const MainParams& mp, int num_cu, hipStream_t stream, int* grid_out) {
+  auto kern = bwd_main_kernel<D, T, BR, CAUSAL, ATOMIC>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, T / 32 * 64, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  long long grid = (long long)num_cu * per_cu;
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  if (grid > mp.n_units) grid = mp.n_units;
+  // Cyclic dQ waits (Shift, Symmetric Shift) need every worker of a head
+  // resident at once; the persistent grid must hold at least one head.
+  if (!ATOMIC && (mp.sched == SCHED_SHIFT || mp.sched == SCHED_SYMMETRIC_SHIFT) && grid < mp.n_workers)
+    return hipErrorInvalidConfiguration;
+  *grid_out = (int)grid;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T / 32 * 64), 0, stream, mp);
+  return hipGetLastError();
+}
+
+template <int D, int T, int BR>
+static hipError_t dispatch_mask(const MainParams& mp, bool causal, bool atomic, int num_cu, hipStream_t s,
+                                int* grid) {
+  if (causal) {
+    return atomic ? launch_main<D, T, BR, true, true>(mp, num_cu, s, grid)
+                  : launch_main<D, T, BR, true, false>(mp, num_cu, s, grid);
+  }
+  return atomic ? launch_main<D, T, BR, false, true>(mp, num_cu, s, grid)
+                : launch_main<D, T, BR, false, false>(mp, num_cu, s, grid);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
+  const long long BH = (long long)a.B * a.H;
+  int* header = (int*)(a.ws + a.lay.header);
+  int* counters = (int*)(a.ws + a.lay.counters);
+  float* lse2 = (float*)(a.ws + a.lay.lse2);
+  float* delta = (float*)(a.ws + a.lay.delta);
+  float* dq_ws = (float*)(a.ws + a.lay.dq_ws);
+  float* park = (float*)(a.ws + a.lay.park);
+
+  PreParams pp;
+  pp.o = (const bf16*)a.o;
+  pp.dout = (const bf16*)a.dout;
+  pp.lse = a.lse;
+  pp.lse2 = lse2;
+  pp.delta = delta;
+  pp.dq_ws = dq_ws;
+  pp.counters = counters;
+  pp.header = header;
+  pp.rows = BH * a.S_pad;
+  pp.S = a.S;
+  pp.S_pad = a.S_pad;
+  pp.n_counters = BH * a.n_qsub;
+  pp.dq_ws_elems = a.atomic ? BH * a.S_pad * a.D : 0;
+  pp.poison = a.atomic ? 0 : a.poison;
+  {
+    const long long want = (pp.rows * (a.D / 8) + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
+    if (a.D == 64) hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3(grid), dim3(256), 0, stream, pp);
+    else hipLaunchKernelGGL(bwd_pre_kernel<128>, dim3(grid), dim3(256), 0, stream, pp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  MainParams mp;
+  mp.q = (const bf16*)a.q;
+  mp.k = (const bf16*)a.k;
+  mp.v = (const bf16*)a.v;
+  mp.dout = (const bf16*)a.dout;
+  mp.dq = (bf16*)a.dq;
+  mp.dk = (bf16*)a.dk;
+  mp.dv = (bf16*)a.dv;
+  mp.lse2 = lse2;
+  mp.delta = delta;
+  mp.dq_ws = dq_ws;
+  mp.park = park;
+  mp.counters = counters;
+  mp.header = header;
+  mp.S = a.S;
+  mp.S_pad = a.S_pad;
+  mp.N = a.N;
+  mp.n_qsub = a.n_qsub;
+  mp.sched = a.atomic ? SCHED_NAIVE : a.sched;
+  mp.n_workers = sched_workers(a.N, mp.sched);
+  mp.n_units = (int)(BH * mp.n_workers);
+  mp.scale = a.scale;
+  mp.scale_log2 = a.scale * 1.4426950408889634f;
+  mp.wait_limit = a.wait_limit;
+
+  int grid = 0;
+  hipError_t e = hipErrorInvalidValue;
+  const bool causal = a.causal != 0, atomic = a.atomic != 0;
+  if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, stream, &grid);
+  else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
+  else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, stream, &grid);
+  else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
+  if (e != hipSuccess) return e;
+
+  if (atomic) {
+    const long long want = (BH * a.S * (a.D / 4) + 255) / 256;
+    const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+    if (a.D == 64)
+      hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
+                         a.S_pad, a.scale);
+    else
+      hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
+                         a.S_pad, a.scale);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace attn

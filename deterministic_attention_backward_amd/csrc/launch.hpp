@@ -1,0 +1,68 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Workgroups that may hold a Symmetric Shift parking slot at once; the
+// persistent grid never exceeds this.
+constexpr int kMaxGrid = 512;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte layout of the backward workspace (every region 256-byte aligned):
+//   header   int32[64]: [0] unit ticket, [1] timeout flag
+//   counters int32[BH * n_qsub]: per (head, query sub-tile) dQ turn counter
+//   lse2     fp32[BH * S_pad]: lse * log2(e), +inf on padding rows
+//   delta    fp32[BH * S_pad]: rowsum(dO * O), 0 on padding rows
+//   dq_ws    fp32[BH * S_pad * D]: dQ accumulator
+//   park     fp32[kMaxGrid * 2 * T * D * 2]: Symmetric Shift only; per workgroup,
+//            one slot per KV tile of its pair, each holding dK and dV
+struct WsLayout {
+  size_t header, counters, lse2, delta, dq_ws, park, total;
+};
+
+inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, bool park) {
+  WsLayout w;
+  size_t off = 0;
+  w.header = off;   off += align256(64 * sizeof(int));
+  w.counters = off; off += align256(size_t(BH) * n_qsub * sizeof(int));
+  w.lse2 = off;     off += align256(size_t(BH) * S_pad * sizeof(float));
+  w.delta = off;    off += align256(size_t(BH) * S_pad * sizeof(float));
+  w.dq_ws = off;    off += align256(size_t(BH) * S_pad * D * sizeof(float));
+  w.park = off;     off += park ? align256(size_t(kMaxGrid) * 2 * T * D * 2 * sizeof(float)) : 0;
+  w.total = off;
+  return w;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float* lse;
+  void *dq, *dk, *dv;
+  char* ws;
+  WsLayout lay;
+  int B, H, S, D, T, BR, N, S_pad, n_qsub;
+  float scale;
+  int causal, sched, atomic;
+  uint32_t wait_limit;
+  int poison;
+};
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  int B, H, S, D, causal;
+  float scale;
+};
+
+// Sub-tile height (query rows per MFMA pass) the backward uses for (D, T).
+inline int bwd_sub_rows(int D, int T) { return (D == 64 && T == 128) ? 128 : 64; }
+
+hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace attn

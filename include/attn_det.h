@@ -1,0 +1,166 @@
+/*
+ * attn_det.h - deterministic attention backward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libattn_det.so. The operation is the backward pass of softmax
+ * attention, dQ/dK/dV from Q, K, V, the forward output O, the upstream
+ * gradient dO and the forward log-sum-exp, computed so that every result is
+ * bit-identical from run to run. The DASH pages (arXiv 2601.21824; Dutch and
+ * Japanese technical summaries §1, English abstract) locate the
+ * nondeterminism of fused attention backward in the floating-point
+ * accumulation of dQ across KV tiles and fix it by accumulating each dQ tile
+ * in a predetermined order; §2.2 of the technical summaries gives the
+ * schedules implemented here.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, o, dout, dq, dk, dv are bfloat16, contiguous, laid out
+ *     [B][H][S][D] (batch, head, position, feature). lse is float32 [B][H][S].
+ *   - Query and key length are both S (self-attention). S >= 1, any value: a
+ *     ragged last tile is masked inside the kernels. D is 64 or 128.
+ *   - mask: ATTN_MASK_FULL, or ATTN_MASK_CAUSAL (key s' visible to query s
+ *     iff s' <= s).
+ *   - scale multiplies q.k before the softmax (usually 1/sqrt(D)).
+ *   - lse is the natural-log log-sum-exp of the scaled (and masked) scores
+ *     of each query row, as written by attn_fwd.
+ *   - All pointers are device pointers owned by the caller; the library never
+ *     allocates or frees device memory. Every pointer must be 16-byte aligned.
+ *   - stream is a hipStream_t (passed as void*; NULL = the default stream).
+ *     Work is enqueued asynchronously; results are valid after the stream is
+ *     synchronised.
+ *   - Every entry point returns an attn_status_t. Argument errors are detected
+ *     on the host before any HIP call and leave device memory untouched.
+ *   - The library keeps no state between calls apart from a per-device cache
+ *     of the compute-unit count and the debug settings below; calls on
+ *     different streams that use different workspaces may run concurrently.
+ */
+#ifndef ATTN_DET_H
+#define ATTN_DET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, bad enum value */
+  ATTN_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement    */
+  ATTN_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required      */
+  ATTN_ERR_ALIGNMENT = -4,     /* a pointer is not 16-byte aligned                */
+  ATTN_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed      */
+  ATTN_ERR_TIMEOUT = -6        /* a dQ ordering wait exceeded its bound            */
+} attn_status_t;
+
+typedef enum { ATTN_MASK_FULL = 0, ATTN_MASK_CAUSAL = 1 } attn_mask_t;
+
+/* dQ schedules: the order in which each worker walks the query tiles and the
+ * order in which each dQ tile is accumulated (see attn_schedule_plan). */
+typedef enum {
+  ATTN_SCHED_NAIVE = 0,          /* ascending query tiles; dQ in KV-ascending order       */
+  ATTN_SCHED_DESCENDING = 1,     /* Descending Q-Tile Iteration (DASH §2.2 A)             */
+  ATTN_SCHED_SHIFT = 2,          /* Shift Scheduling, full mask (DASH §2.2 B)             */
+  ATTN_SCHED_SYMMETRIC_SHIFT = 3 /* Symmetric Shift, causal mask, even tile count (§2.2 B)*/
+} attn_schedule_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd - attention forward, used to produce the backward's O and LSE.
+ *   o   = softmax(scale * q k^T [masked]) v        bf16 [B][H][S][D]
+ *   lse = log(sum_j exp(scale * q_i . k_j))        fp32 [B][H][S]
+ * Deterministic (fixed accumulation order). Not a tuned kernel.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, float scale, int mask, void* stream);
+
+/*
+ * attn_bwd_tile - the KV/query tile edge T the backward will use.
+ *   tile_request = 0 lets the library choose (64 when S <= 256, else 128);
+ *   64 or 128 forces that edge. Returns T (> 0) or a negative status.
+ *   The head is cut into N = ceil(S / T) query tiles and N KV tiles.
+ */
+int attn_bwd_tile(int S, int D, int tile_request);
+
+/*
+ * attn_bwd_workspace_size - bytes of device workspace a backward call needs.
+ * The workspace holds the fp32 dQ accumulator (B*H*ceil(S/T)*T*D floats), the
+ * per-row softmax terms, the dQ ordering counters and, for Symmetric Shift,
+ * the parking area for a worker's second set of dK/dV accumulators.
+ * Returns 0 for invalid arguments (then the call itself reports why).
+ */
+size_t attn_bwd_workspace_size(int B, int H, int S, int D, int mask, int schedule, int tile_request);
+
+/*
+ * attn_bwd_deterministic - bit-reproducible attention backward.
+ *   In:  q, k, v, o, dout (bf16 [B][H][S][D]), lse (fp32 [B][H][S]).
+ *   Out: dq, dk, dv (bf16 [B][H][S][D]); overwritten, no accumulation.
+ *   Each workgroup owns one KV tile (two for Symmetric Shift) and keeps its
+ *   dK/dV in registers; dQ tile i is accumulated in fp32 in the order the
+ *   schedule fixes, each contributor waiting for its turn on a per-tile
+ *   counter. The dQ accumulation uses no floating-point atomics.
+ *   schedule: attn_schedule_t. SHIFT needs ATTN_MASK_FULL; SYMMETRIC_SHIFT
+ *   needs ATTN_MASK_CAUSAL and an even tile count; other combinations return
+ *   ATTN_ERR_UNSUPPORTED.
+ *   workspace: device memory of at least attn_bwd_workspace_size(...) bytes,
+ *   owned by the caller; contents need not be initialised and are scratch
+ *   after the call. Concurrent calls must use distinct workspaces.
+ *   The output for a given input and (schedule, tile) is the same bit pattern
+ *   on every run. Different schedules may differ in the last bits.
+ */
+int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, int mask, int schedule,
+                           void* dq, void* dk, void* dv, int B, int H, int S, int D,
+                           float scale, int tile_request, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_nondeterministic - the same backward with dQ accumulated by
+ * hardware fp32 atomic adds in whatever order the hardware performs them (the
+ * non-deterministic counterpart the DASH abstract compares against). Ascending
+ * query-tile walk; no ordering waits. Workspace as for the deterministic call
+ * with schedule ATTN_SCHED_NAIVE.
+ */
+int attn_bwd_nondeterministic(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, int mask,
+                              void* dq, void* dk, void* dv, int B, int H, int S, int D,
+                              float scale, int tile_request, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_check - wait for `stream`, then report whether a deterministic call
+ * that used `workspace` tripped the bound on a dQ ordering wait
+ * (ATTN_ERR_TIMEOUT), else ATTN_OK. Host-blocking.
+ */
+int attn_bwd_check(const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_schedule_plan - host-only export of one head's schedule (no HIP call).
+ *   n_tiles = N; mask, schedule as above.
+ *   Writes int32 values to out: [n_workers, n_tasks, then for every task, in
+ *   (worker, step) order, the five values worker, step, q_tile, kv_tile, rank].
+ *   *needed (if not NULL) receives the number of int32 values required.
+ *   out may be NULL to query the size; otherwise out_len must be >= *needed
+ *   or ATTN_ERR_INVALID_ARG is returned.
+ */
+int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t out_len,
+                       size_t* needed);
+
+/*
+ * attn_debug_set_wait_limit - bound (in polling iterations, each one a
+ * counter load plus a short sleep) on a single dQ ordering wait; 0 restores
+ * the default (about 2^24). When a wait reaches the bound the workgroup
+ * records ATTN_ERR_TIMEOUT in the workspace, stops waiting and finishes
+ * normally; attn_bwd_check reports it. poison_counter != 0 makes the next
+ * deterministic calls start one dQ counter at an unreachable value so that the
+ * bound is certain to trip (used to test the timeout path). Process-wide,
+ * not thread-safe; for tests only.
+ */
+void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DET_H */

@@ -175,3 +175,29 @@ def compare(x, y):
     ny = float(np.sqrt((y * y).sum()))
     rel = float(np.sqrt((d * d).sum())) / ny if ny > 0 else float(np.sqrt((d * d).sum()))
     return max_abs, rel
+
+
+def backward_rows_head(q, k, v, o, do, lse, causal: bool, scale: float, q_rows, k_rows):
+    """The backward of one head restricted to chosen rows (for large S).
+
+    Returns (dq[q_rows], dk[k_rows], dv[k_rows]) from the same formulas as
+    backward_head: a dQ row needs its own row of P' and dS; a dK/dV row needs
+    one column of P' and dS, hence every query's LSE and Delta. O(S*D) per row.
+    """
+    S = q.shape[0]
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    dlt = delta(o, do)
+    keys = np.arange(S)
+    # rows of dS for the chosen queries
+    vis_q = (keys[None, :] <= q_rows[:, None]) if causal else np.ones((q_rows.size, S), dtype=bool)
+    p_q = np.where(vis_q, np.exp(scale * (q[q_rows] @ k.T) - lse[q_rows, None]), 0.0)
+    ds_q = p_q * (do[q_rows] @ v.T - dlt[q_rows, None])
+    dq = scale * (ds_q @ k)
+    # columns of P' and dS for the chosen keys
+    vis_k = (keys[:, None] >= k_rows[None, :]) if causal else np.ones((S, k_rows.size), dtype=bool)
+    p_k = np.where(vis_k, np.exp(scale * (q @ k[k_rows].T) - lse[:, None]), 0.0)
+    ds_k = p_k * (do @ v[k_rows].T - dlt[:, None])
+    dv = p_k.T @ do
+    dk = scale * (ds_k.T @ q)
+    return dq, dk, dv

@@ -282,3 +282,18 @@ def test_pins_catch_planted_mistakes(kind):
                 failed = True
     assert failed
     assert any(not np.allclose(a, b) for a, b in zip(good, bad))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_sampled_backward_matches_full(causal):
+    S, D = 150, 8
+    q, k, v, do = (rnd((S, D), s) for s in (111, 112, 113, 114))
+    c = 0.4
+    o, lse = A.forward_head(q, k, v, causal, c)
+    dq, dk, dv = A.backward_head(q, k, v, o, do, lse, causal, c)
+    qr = [0, 1, 77, 149]
+    kr = [0, 5, 148, 149]
+    sq, sk, sv = A.backward_rows_head(q, k, v, o, do, lse, causal, c, qr, kr)
+    assert np.allclose(sq, dq[qr], rtol=1e-12, atol=1e-13)
+    assert np.allclose(sk, dk[kr], rtol=1e-12, atol=1e-13)
+    assert np.allclose(sv, dv[kr], rtol=1e-12, atol=1e-13)
