@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the deterministic attention backward on one MI355X.
+
+One step = one call of the deterministic backward (pre-pass + main tile
+kernel with the ordered dQ reduction; the last contributor writes dq), on
+synthetic bf16 inputs already resident in HBM. The default workload is the
+full-mask B=4, H=16, S=2048, D=128 case. Every deterministic schedule valid
+for the mask is timed, then the atomic-dQ variant; `value` is the fastest
+deterministic schedule's throughput under the FLOP convention
+2.5 * 4 * B * H * S^2 * D (halved for a causal mask).
+
+Printed (one JSON line on stdout): the metric, value (TFLOP/s), % of the bf16
+dense MFMA peak, the deterministic/non-deterministic ratio, per-schedule
+numbers, the roofline of the main tile kernel (its duration taken with HIP
+events recorded around its launch on its own stream) and the CPU oracle's
+throughput on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+METRIC = "deterministic attn-bwd TFLOPS (bf16) + % MFMA peak + ratio vs non-det kernel"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent pairs through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def time_variant(fn, steps, warmup, torch, events, lib):
+    """Wall time of `steps` calls (synchronised both sides) and the mean main-kernel time."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pairs = [(events.create(), events.create()) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        lib.attn_set_timing_events(a, b)
+        fn()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lib.attn_set_timing_events(None, None)
+    kern = [events.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        events.destroy(a)
+        events.destroy(b)
+    return wall / steps * 1e3, sum(kern) / len(kern)
+
+
+def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
+    """The float64 oracle backward on whole heads of the same workload, time-bounded."""
+    import numpy as np
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    B, H = w.B, w.H
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < B * H:
+        b, h = divmod(heads, H)
+        f = lambda t: t[b, h].to(dtype=__import__("torch").float64).numpy()
+        q, k, v, do = (f(inputs[n]) for n in ("q", "k", "v", "do"))
+        A.backward_head(q, k, v, f(o_cpu), do, lse_cpu[b, h].double().numpy(), w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops / (B * H) * heads
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {B * H} heads of the same workload (float64 backward from the HIP forward's O/LSE), "
+                  f"{dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--schedules", default="", help="comma list; default: every schedule valid for the mask")
+    ap.add_argument("--no-nondet", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle leg (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attn_inputs
+    import deterministic_attention_backward_amd as dab
+    from deterministic_attention_backward_amd import _lib
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible: the benchmark needs an MI355X")
+    lib = _lib.load()
+    events = HipEvents()
+    w = attn_inputs.WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.describe()} seed={w.seed}")
+    x = attn_inputs.draw_workload(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = dab.fwd(q, k, v, w.causal, w.scale)
+    torch.cuda.synchronize()
+    T = dab.tile(w.S, w.D, w.tile)
+    N = -(-w.S // T)
+
+    if args.schedules:
+        scheds = args.schedules.split(",")
+    else:
+        scheds = ["naive", "descending"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else []) + \
+                 ([] if w.causal else ["shift"])
+    out = tuple(torch.empty_like(q) for _ in range(3))
+    results = {}
+    for s in scheds:
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile)
+        fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
+        ms, kms = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        dab.check_workspace(ws)
+        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12}
+        log(f"  {s:16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {results[s]['tflops']:7.1f} TFLOP/s")
+        del ws
+    nondet = None
+    if not args.no_nondet:
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile)
+        fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
+        ms, kms = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12}
+        log(f"  {'atomic (non-det)':16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {nondet['tflops']:7.1f} TFLOP/s")
+        del ws
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nbytes} bytes read + {nbytes} bytes written per copy, 3 copies")
+
+    best = min(results, key=lambda s: results[s]["ms"])
+    r = results[best]
+    achieved = w.flops / (r["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}", "schedule": best, "tile": T, "n_tiles": N,
+                   "seed": w.seed, "flops_per_step": w.flops},
+        "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,
+        "schedules": {s: {"ms": round(v["ms"], 4), "kernel_ms": round(v["kernel_ms"], 4),
+                          "tflops": round(v["tflops"], 2)} for s, v in results.items()},
+        "nondet": {k2: round(v2, 4) for k2, v2 in nondet.items()} if nondet else None,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "bwd_main_kernel", "kernel_ms": round(r["kernel_ms"], 4)},
+    }
+    if args.cpu_seconds > 0:
+        x_cpu = {n: x[n] for n in ("q", "k", "v", "do")}
+        line["cpu_baseline"] = cpu_baseline(w, x_cpu, o.cpu(), lse.cpu(), args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,7 @@ EXPORTS = (
     "attn_bwd_check",
     "attn_schedule_plan",
     "attn_debug_set_wait_limit",
+    "attn_set_timing_events",
 )
 
 _lib = None
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.attn_schedule_plan.restype = i
     lib.attn_debug_set_wait_limit.argtypes = [ctypes.c_uint32, i]
     lib.attn_debug_set_wait_limit.restype = None
+    lib.attn_set_timing_events.argtypes = [vp, vp]
+    lib.attn_set_timing_events.restype = None
     _lib = lib
     return lib
 

@@ -17,6 +17,7 @@ namespace {
 constexpr uint32_t kDefaultWaitLimit = 1u << 24;
 uint32_t g_wait_limit = kDefaultWaitLimit;
 int g_poison = 0;
+hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 constexpr int kMaxDevices = 64;
 int g_num_cu[kMaxDevices];  // 0 = not queried yet
@@ -112,6 +113,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   a.atomic = deterministic ? 0 : 1;
   a.wait_limit = g_wait_limit;
   a.poison = g_poison;
+  a.ev_before = g_ev_before;
+  a.ev_after = g_ev_after;
   const hipError_t e = launch_bwd(a, num_cu, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidConfiguration) return ATTN_ERR_UNSUPPORTED;
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -225,6 +228,15 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
     }
   }
   return ATTN_OK;
+}
+
+void attn_set_timing_events(void* before, void* after) {
+  if (before && after) {
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+  } else {
+    g_ev_before = g_ev_after = nullptr;
+  }
 }
 
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter) {

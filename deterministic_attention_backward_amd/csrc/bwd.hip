@@ -12,8 +12,9 @@
 // Shift). The unit walks its tasks (query tile i, KV tile j) in the order the
 // schedule fixes, accumulates dK_j/dV_j in MFMA accumulators and, per query
 // sub-tile, hands its dQ partial to the fp32 dQ workspace in the schedule's
-// order: wait until the sub-tile's counter equals r(i, j), add, publish,
-// increment. The last contributor converts to bf16 and writes dq directly.
+// order: wait until the sub-tile's counter equals r(i, j), add, then (one
+// sub-tile later, when the adds have long completed) increment the counter. A
+// post-pass converts the fp32 accumulator to bf16 dq.
 #include "common.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
@@ -71,11 +72,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
 
 // --------------------------------------------------------------------------------------
 // main kernel
+//
+// Workgroup = T/32 waves; wave w owns keys 32w..32w+31 of the current KV tile.
+// Registers hold, for the whole unit: this wave's K and V rows as the B
+// operands of S = Q K^T and dP = dO V^T, the K columns it needs as the B
+// operand of dQ = dS K, and the dK/dV accumulators. Per query sub-tile
+// (BR rows) LDS holds Q and dO twice: row-major (A operands of S and dP) and
+// transposed with the queries of every 16-row group permuted so that one
+// 16-byte read yields a lane's eight k-values of the dV/dK B operand in the
+// order the P/dS accumulators supply them. dS goes to LDS transposed (one
+// 8-byte write per accumulator quad) and comes back through the gfx950
+// transpose read as the A operand of dQ.
 
 struct MainParams {
   const bf16 *q, *k, *v;
   const bf16* dout;
-  bf16 *dq, *dk, *dv;
+  bf16 *dk, *dv;
   const float *lse2, *delta;
   float *dq_ws, *park;
   int *counters, *header;
@@ -84,31 +96,49 @@ struct MainParams {
   uint32_t wait_limit;
 };
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// supplies the address of a 4-element row chunk and receives element i % 4 of
+// the chunks supplied by lanes 4e + i / 4, e = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// quads of each 16-query group in transposed LDS rows are stored in the order 0, 2, 1, 3
+__device__ __forceinline__ int quad_pos(int qg) { return 16 * (qg >> 2) + 4 * ((qg & 1) * 2 + ((qg >> 1) & 1)); }
+
 template <int D, int T, int BR, bool CAUSAL, bool ATOMIC>
 __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) {
-  constexpr int NW = T / 32;       // waves; wave w owns keys 32w..32w+31 of the KV tile
+  constexpr int NW = T / 32;
   constexpr int NT = NW * 64;
-  constexpr int DP = D + 8;        // padded LDS row lengths (bf16 elements)
-  constexpr int BRP = BR + 8;
-  constexpr int TP = T + 8;
-  constexpr int KC = D / 16;       // 16-wide k-chunks over the feature dimension
+  constexpr int DP = D + 8;        // row-major Q/dO rows (bf16 elements)
+  constexpr int BRP = BR + 8;      // transposed Q/dO rows
+  constexpr int TP = T + 8;        // transposed K rows
+  constexpr int SP = BR + 4;       // transposed dS rows
+  constexpr int KC = D / 16;       // k-chunks over the feature dimension
   constexpr int ND = D / 32;       // 32-wide feature blocks
   constexpr int MB = BR / 32;      // 32-row query blocks per sub-tile
   constexpr int NSUB = T / BR;     // query sub-tiles per task
-  constexpr int QB = MB * ND;      // 32x32 blocks of a dQ sub-tile
-  constexpr int QBW = QB / NW;     // ... per wave
+  constexpr int QBW = MB * ND / NW;             // dQ 32x32 blocks per wave
+  constexpr int NCOL = ND >= NW ? ND / NW : 1;  // ... in this many feature columns
+  constexpr int NROW = QBW / NCOL;              // ... and this many query rows
+  constexpr int TC = T / 16;       // k-chunks over the keys
   constexpr int GROUPS = (BR / 4) * (D / 8);  // staging pieces: 4 rows x 8 features
   constexpr int GPT = GROUPS / NT;
-  static_assert(QB % NW == 0 && GROUPS % NT == 0 && T % BR == 0, "tile shape");
+  static_assert(QBW * NW == MB * ND && GROUPS % NT == 0 && T % BR == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BR * DP];    // Q sub-tile [row][d]
-  __shared__ __attribute__((aligned(16))) bf16 sQT[D * BRP];   // Q sub-tile [d][row]
-  __shared__ __attribute__((aligned(16))) bf16 sO[BR * DP];    // dO sub-tile [row][d]
-  __shared__ __attribute__((aligned(16))) bf16 sOT[D * BRP];   // dO sub-tile [d][row]
-  __shared__ __attribute__((aligned(16))) bf16 sKT[D * TP];    // K tile [d][key]
-  __shared__ __attribute__((aligned(16))) bf16 sdS[BR * TP];   // dS sub-tile [row][key]
-  __shared__ __attribute__((aligned(16))) float sL[BR];        // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sDl[BR];       // Delta
+  __shared__ __attribute__((aligned(16))) bf16 sQ[BR * DP];
+  __shared__ __attribute__((aligned(16))) bf16 sO[BR * DP];
+  __shared__ __attribute__((aligned(16))) bf16 sQT[D * BRP];
+  __shared__ __attribute__((aligned(16))) bf16 sOT[D * BRP];
+  __shared__ __attribute__((aligned(16))) bf16 sKT[D * TP];
+  __shared__ __attribute__((aligned(16))) bf16 sdST[T * SP];
+  __shared__ __attribute__((aligned(16))) float sL[BR];
+  __shared__ __attribute__((aligned(16))) float sDl[BR];
   __shared__ int sUnit;
 
   const int tid = threadIdx.x;
@@ -118,16 +148,20 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
   const int hh = lane >> 5;
   const int S = p.S;
 
-  bf16x8 Kr[KC], Vr[KC];           // this wave's 32 keys as MFMA B operands
-  f32x16 dKa[ND], dVa[ND];         // dK, dV accumulators of the current KV tile
+  bf16x8 Kr[KC], Vr[KC];           // B operands of S and dP (this wave's keys)
+  bf16x8 Kd[NCOL][TC];             // B operand of dQ (all keys, this wave's columns)
+  f32x16 dKa[ND], dVa[ND];
   u32x4 stq[GPT][4], sto[GPT][4];  // staged next sub-tile
   float stl = 0.0f, std_ = 0.0f;
+
+  auto col_of = [&](int kc) { return ND >= NW ? w * NCOL + kc : w % ND; };
+  auto row_of = [&](int kr) { return ND >= NW ? kr : w / ND + kr * (NW / ND); };
 
   auto stage_load = [&](int bh, int qrow0) {
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tid + g * NT;
-      const int qg = gi / (D / 8), dg = gi % (D / 8);
+      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = qrow0 + qg * 4 + rr;
@@ -152,28 +186,23 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tid + g * NT;
-      const int qg = gi / (D / 8), dg = gi % (D / 8);
+      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         *(u32x4*)&sQ[(qg * 4 + rr) * DP + dg * 8] = stq[g][rr];
         *(u32x4*)&sO[(qg * 4 + rr) * DP + dg * 8] = sto[g][rr];
       }
-      bf16x8 qv[4], ov[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        qv[rr] = __builtin_bit_cast(bf16x8, stq[g][rr]);
-        ov[rr] = __builtin_bit_cast(bf16x8, sto[g][rr]);
-      }
+      const int pos = quad_pos(qg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         bf16x4 tq, to;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          tq[rr] = qv[rr][e];
-          to[rr] = ov[rr][e];
+          tq[rr] = __builtin_bit_cast(bf16x8, stq[g][rr])[e];
+          to[rr] = __builtin_bit_cast(bf16x8, sto[g][rr])[e];
         }
-        *(bf16x4*)&sQT[(dg * 8 + e) * BRP + qg * 4] = tq;
-        *(bf16x4*)&sOT[(dg * 8 + e) * BRP + qg * 4] = to;
+        *(bf16x4*)&sQT[(dg * 8 + e) * BRP + pos] = tq;
+        *(bf16x4*)&sOT[(dg * 8 + e) * BRP + pos] = to;
       }
     }
     if (tid < BR) {
@@ -182,6 +211,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
     }
   };
 
+  // K/V of KV tile kv into registers (and K^T through LDS for the dQ operand)
   auto load_kv = [&](int bh, int kv) {
     const int key = kv * T + 32 * w + l32;
 #pragma unroll
@@ -200,6 +230,13 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKT[(16 * c + 8 * hh + e) * TP + 32 * w + l32] = Kr[c][e];
     }
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < NCOL; ++kc) {
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+        Kd[kc][c] = *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
+    }
   };
 
   auto finalize_kv = [&](int bh, int kv) {
@@ -217,7 +254,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
     }
   };
 
-  // Symmetric Shift parking: one slot per (workgroup, tile of the pair).
+  // Symmetric Shift parking: one slot per (workgroup, tile of the pair)
   auto park_acc = [&](int slot, bool load) {
     float* base = p.park + ((size_t)blockIdx.x * 2 + slot) * (size_t)(2 * ND * 16 * NT);
 #pragma unroll
@@ -249,7 +286,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
     const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
     const int total = ntasks * NSUB;
 
-    // the (at most two) KV tiles this unit owns and the last task of each
+    // the (at most two) KV tiles of this unit and the last task of each
     int tileA = -1, tileB = -1, lastA = -1, lastB = -1;
     for (int t = 0; t < ntasks; ++t) {
       const int kv = sched_task(p.N, CAUSAL, p.sched, wk, t).kv;
@@ -263,6 +300,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
     }
     int cur_kv = -1;
     bool parkedA = false, parkedB = false;
+    int pend = -1;  // counter whose increment is still owed (its RMWs are in flight)
 
     {
       const Task t0 = sched_task(p.N, CAUSAL, p.sched, wk, 0);
@@ -283,15 +321,14 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
       if (kj != cur_kv) {
         if (cur_kv >= 0) {
           const bool isA = (cur_kv == tileA);
-          const int last = isA ? lastA : lastB;
-          if (t <= last) {
+          if (t <= (isA ? lastA : lastB)) {
             park_acc(isA ? 0 : 1, false);
             if (isA) parkedA = true; else parkedB = true;
           } else {
             finalize_kv(bh, cur_kv);
           }
         }
-        __syncthreads();  // every wave is done reading sKT
+        __syncthreads();
         load_kv(bh, kj);
         const bool isA = (kj == tileA);
         if (isA ? parkedA : parkedB) {
@@ -307,14 +344,15 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
         cur_kv = kj;
       }
 
-      const int q_base = qi * T + sidx * BR;   // first query row of this sub-tile
+      const int q_base = qi * T + sidx * BR;
       const int kv_base = kj * T;
-      __syncthreads();  // staged sub-tile and sKT visible
+      __syncthreads();  // staged sub-tile visible
 
-      // ---- S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q
+      // ---- S = Q K^T, dP = dO V^T, P, dS; dV += P^T dO, dK += dS^T Q
       const int key_g = kv_base + 32 * w + l32;
       const bool key_ok = key_g < S;
-#pragma unroll
+      const bool need_mask = (CAUSAL && qi == kj) || (kv_base + T > S);
+#pragma unroll 1
       for (int m = 0; m < MB; ++m) {
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -324,131 +362,131 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
           s = mfma32(qa, Kr[c], s);
           dp = mfma32(oa, Vr[c], dp);
         }
+        if (need_mask) {  // diagonal tile of a causal mask, or the ragged last KV tile
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
-          const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
+            const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int i = 4 * a + b;
-            const int q_g = q_base + 32 * m + 8 * a + 4 * hh + b;
-            float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
-            const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
-            pv = vis ? pv : 0.0f;
-            s[i] = pv;
-            dp[i] = pv * (dp[i] - D4[b]);
+            for (int b = 0; b < 4; ++b) {
+              const int i = 4 * a + b;
+              const int q_g = q_base + 32 * m + 8 * a + 4 * hh + b;
+              float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+              const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
+              pv = vis ? pv : 0.0f;
+              s[i] = pv;
+              dp[i] = pv * (dp[i] - D4[b]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
+            const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const int i = 4 * a + b;
+              const float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+              s[i] = pv;
+              dp[i] = pv * (dp[i] - D4[b]);
+            }
           }
         }
         const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
         const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
+        // dS^T: four consecutive queries per 8-byte write
+        bf16* drow = &sdST[(32 * w + l32) * SP + 32 * m + 4 * hh];
+        *(bf16x4*)(drow + 0) = __builtin_shufflevector(db0, db0, 0, 1, 2, 3);
+        *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
+        *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
+        *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
 #pragma unroll
         for (int n = 0; n < ND; ++n) {
-          const bf16* ro = &sOT[(32 * n + l32) * BRP + 32 * m + 4 * hh];
-          const bf16* rq = &sQT[(32 * n + l32) * BRP + 32 * m + 4 * hh];
-          const bf16x8 ob0 = cat44(*(const bf16x4*)ro, *(const bf16x4*)(ro + 8));
-          const bf16x8 ob1 = cat44(*(const bf16x4*)(ro + 16), *(const bf16x4*)(ro + 24));
-          const bf16x8 qb0 = cat44(*(const bf16x4*)rq, *(const bf16x4*)(rq + 8));
-          const bf16x8 qb1 = cat44(*(const bf16x4*)(rq + 16), *(const bf16x4*)(rq + 24));
-          dVa[n] = mfma32(pb0, ob0, dVa[n]);
-          dVa[n] = mfma32(pb1, ob1, dVa[n]);
-          dKa[n] = mfma32(db0, qb0, dKa[n]);
-          dKa[n] = mfma32(db1, qb1, dKa[n]);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 32 * m + 8 * (i / 4) + 4 * hh + (i % 4);
-          sdS[row * TP + 32 * w + l32] = (i < 8) ? db0[i] : db1[i - 8];
+          const int ro = (32 * n + l32) * BRP + 32 * m + 8 * hh;
+          dVa[n] = mfma32(pb0, *(const bf16x8*)&sOT[ro], dVa[n]);
+          dVa[n] = mfma32(pb1, *(const bf16x8*)&sOT[ro + 16], dVa[n]);
+          dKa[n] = mfma32(db0, *(const bf16x8*)&sQT[ro], dKa[n]);
+          dKa[n] = mfma32(db1, *(const bf16x8*)&sQT[ro + 16], dKa[n]);
         }
       }
-      __syncthreads();  // sdS complete; staged Q/dO no longer read
+      wait_vmem();      // this wave's earlier dQ RMWs and staging loads have completed
+      __syncthreads();  // dS^T complete; staged Q/dO no longer read; all earlier RMWs done
 
+      if (!ATOMIC && pend >= 0 && tid == 0)
+        __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pend = -1;
       if (idx + 1 < total) {
         stage_store();
         if (idx + 2 < total) {
-          const int t2 = (idx + 2) / NSUB;
-          const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, t2);
+          const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, (idx + 2) / NSUB);
           stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
         }
       }
 
-      // ---- dQ partial = dS K for this wave's 32x32 blocks of the sub-tile
-      f32x16 dqa[QBW];
-#pragma unroll
-      for (int bi = 0; bi < QBW; ++bi) {
-        const int b = w + bi * NW;
-        const int mb = b / ND, nb = b % ND;
-        f32x16 acc = zero16();
-#pragma unroll
-        for (int c = 0; c < T / 16; ++c) {
-          const bf16x8 a = *(const bf16x8*)&sdS[(32 * mb + l32) * TP + 16 * c + 8 * hh];
-          const bf16x8 kb = *(const bf16x8*)&sKT[(32 * nb + l32) * TP + 16 * c + 8 * hh];
-          acc = mfma32(a, kb, acc);
-        }
-        dqa[bi] = acc;
-      }
-
-      // ---- hand the partial to dQ tile qi, sub-tile sidx
+      // ---- dQ partial of this sub-tile and its ordered hand-off
+      const int cidx = bh * p.n_qsub + qi * NSUB + sidx;
+      const int r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, qi, kj);
+      const bool last = ATOMIC ? true : (r == sched_contributors(p.N, CAUSAL, qi) - 1);
+      int seen = r;
+      if (!ATOMIC && r > 0 && tid == 0)  // poll early; checked after the first dQ block
+        seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;
-      if (ATOMIC) {
 #pragma unroll
-        for (int bi = 0; bi < QBW; ++bi) {
-          const int b = w + bi * NW;
-          const int mb = b / ND, nb = b % ND;
+      for (int kc = 0; kc < NCOL; ++kc) {
+#pragma unroll 1
+        for (int kr = 0; kr < NROW; ++kr) {
+          const int nb = col_of(kc), mb = row_of(kr);
+          f32x16 acc = zero16();
+          const int grp = lane >> 4, gi = lane & 15;
+          const bf16* base = &sdST[(8 * (grp >> 1) + (gi >> 2)) * SP + 32 * mb + 16 * (grp & 1) + 4 * (gi & 3)];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 32 * mb + 8 * (i / 4) + 4 * hh + (i % 4);
-            unsafeAtomicAdd(wsrow + (size_t)row * D + 32 * nb + l32, dqa[bi][i]);
+          for (int c = 0; c < TC; ++c) {
+            const bf16x8 a = cat44(lds_read_tr(base + 16 * c * SP), lds_read_tr(base + (16 * c + 4) * SP));
+            acc = mfma32(a, Kd[kc][c], acc);
           }
-        }
-      } else {
-        const int cidx = bh * p.n_qsub + qi * NSUB + sidx;
-        const int r = sched_rank(p.N, CAUSAL, p.sched, qi, kj);
-        const bool last = (r == sched_contributors(p.N, CAUSAL, qi) - 1);
-        if (r > 0) {
-          if (tid == 0) {
-            uint32_t it = 0;
-            while (__hip_atomic_load(&p.counters[cidx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != r) {
-              if (++it >= p.wait_limit) {
-                __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
+          if (!ATOMIC && r > 0 && kc == 0 && kr == 0) {
+            // Turn-taking: wait until the previous contributor's RMWs are done.
+            if (tid == 0) {
+              uint32_t it = 0;
+              while (seen != r) {
+                if (++it >= p.wait_limit) {
+                  __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
-              __builtin_amdgcn_s_sleep(2);
             }
+            __syncthreads();
           }
-          __syncthreads();
-        }
-#pragma unroll
-        for (int bi = 0; bi < QBW; ++bi) {
-          const int b = w + bi * NW;
-          const int mb = b / ND, nb = b % ND;
+          // Every access to the dQ accumulator is a device-scope atomic RMW
+          // (executed where such operations are coherent across XCDs); the
+          // counters only serialise them, so each element receives the same
+          // fp32 additions in the same order on every run.
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = 32 * mb + 8 * (i / 4) + 4 * hh + (i % 4);
             float* a = wsrow + (size_t)row * D + 32 * nb + l32;
-            float val = dqa[bi][i];
-            if (r > 0) val = *a + val;
-            if (last) {
-              if (q_base + row < S)
-                p.dq[((size_t)bh * S + q_base + row) * D + 32 * nb + l32] = to_bf16(val * p.scale);
-            } else {
-              *a = val;
-            }
+            if (!ATOMIC && r == 0)
+              __hip_atomic_exchange(a, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+              __hip_atomic_fetch_add(a, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
-        if (!last) {
-          wait_vmem();      // this wave's dQ stores have completed
-          __syncthreads();  // ... and so have every other wave's
-          if (tid == 0)  // next turn; an increment keeps a poisoned counter out of reach
-            __hip_atomic_fetch_add(&p.counters[cidx], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
       }
+      if (!ATOMIC && !last) pend = cidx;
+    }
+    if (pend >= 0) {  // the unit's last hand-off
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (cur_kv >= 0) finalize_kv(bh, cur_kv);
   }
 }
 
 // --------------------------------------------------------------------------------------
-// post-pass (atomic variant): dq = bf16(scale * dQ accumulator)
+// post-pass: dq = bf16(scale * dQ accumulator)
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, long long BH, int S,
@@ -540,7 +578,6 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.k = (const bf16*)a.k;
   mp.v = (const bf16*)a.v;
   mp.dout = (const bf16*)a.dout;
-  mp.dq = (bf16*)a.dq;
   mp.dk = (bf16*)a.dk;
   mp.dv = (bf16*)a.dv;
   mp.lse2 = lse2;
@@ -563,13 +600,21 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   int grid = 0;
   hipError_t e = hipErrorInvalidValue;
   const bool causal = a.causal != 0, atomic = a.atomic != 0;
+  if (a.ev_before && a.ev_after) {
+    e = hipEventRecord(a.ev_before, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, stream, &grid);
   else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
   else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, stream, &grid);
   else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
   if (e != hipSuccess) return e;
+  if (a.ev_before && a.ev_after) {
+    e = hipEventRecord(a.ev_after, stream);
+    if (e != hipSuccess) return e;
+  }
 
-  if (atomic) {
+  {
     const long long want = (BH * a.S * (a.D / 4) + 255) / 256;
     const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
     if (a.D == 64)

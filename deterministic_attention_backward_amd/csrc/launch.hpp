@@ -49,6 +49,7 @@ struct BwdArgs {
   int causal, sched, atomic;
   uint32_t wait_limit;
   int poison;
+  hipEvent_t ev_before, ev_after;  // optional: recorded around the main kernel
 };
 
 struct FwdArgs {

@@ -159,6 +159,16 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
  */
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
 
+/*
+ * attn_set_timing_events - profiling hook. When both arguments are non-NULL
+ * hipEvent_t handles (created by the caller), every following backward call
+ * records `before` on its stream immediately before launching its main tile
+ * kernel and `after` immediately after it, so hipEventElapsedTime(before,
+ * after) is that kernel's duration. NULL, NULL turns the hook off.
+ * Process-wide, not thread-safe; for benchmarks only.
+ */
+void attn_set_timing_events(void* before, void* after);
+
 #ifdef __cplusplus
 }
 #endif
