@@ -157,28 +157,28 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
   auto col_of = [&](int kc) { return ND >= NW ? w * NCOL + kc : w % ND; };
   auto row_of = [&](int kr) { return ND >= NW ? kr : w / ND + kr * (NW / ND); };
 
+  // Rows past the end of the sequence are read as copies of the last row: the
+  // masks give them P = 0 exactly, so a finite duplicate contributes nothing.
   auto stage_load = [&](int bh, int qrow0) {
+    const bf16* qh = p.q + (size_t)bh * S * D;     // uniform head bases
+    const bf16* oh = p.dout + (size_t)bh * S * D;
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tid + g * NT;
       const int qg = gi % (BR / 4), dg = gi / (BR / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int row = qrow0 + qg * 4 + rr;
-        if (row < S) {
-          const size_t off = ((size_t)bh * S + row) * D + dg * 8;
-          stq[g][rr] = *(const u32x4*)(p.q + off);
-          sto[g][rr] = *(const u32x4*)(p.dout + off);
-        } else {
-          stq[g][rr] = u32x4{0u, 0u, 0u, 0u};
-          sto[g][rr] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const int row = min(qrow0 + qg * 4 + rr, S - 1);
+        const unsigned off = 2u * (unsigned)(row * D + dg * 8);
+        stq[g][rr] = *at_bytes((const u32x4*)qh, off);
+        sto[g][rr] = *at_bytes((const u32x4*)oh, off);
       }
     }
     if (tid < BR) {
-      const size_t off = (size_t)bh * p.S_pad + qrow0 + tid;
-      stl = p.lse2[off];
-      std_ = p.delta[off];
+      const float* lh = p.lse2 + (size_t)bh * p.S_pad;
+      const float* dh = p.delta + (size_t)bh * p.S_pad;
+      stl = *at_bytes(lh, 4u * (unsigned)(qrow0 + tid));
+      std_ = *at_bytes(dh, 4u * (unsigned)(qrow0 + tid));
     }
   };
 
@@ -213,20 +213,14 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
 
   // K/V of KV tile kv into registers (and K^T through LDS for the dQ operand)
   auto load_kv = [&](int bh, int kv) {
-    const int key = kv * T + 32 * w + l32;
+    const int key = min(kv * T + 32 * w + l32, S - 1);  // keys past the end are masked
+    const bf16* kh = p.k + (size_t)bh * S * D;
+    const bf16* vh = p.v + (size_t)bh * S * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      if (key < S) {
-        const size_t off = ((size_t)bh * S + key) * D + 16 * c + 8 * hh;
-        Kr[c] = *(const bf16x8*)(p.k + off);
-        Vr[c] = *(const bf16x8*)(p.v + off);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          Kr[c][e] = (bf16)0.0f;
-          Vr[c][e] = (bf16)0.0f;
-        }
-      }
+      const unsigned off = 2u * (unsigned)(key * D + 16 * c + 8 * hh);
+      Kr[c] = *at_bytes((const bf16x8*)kh, off);
+      Vr[c] = *at_bytes((const bf16x8*)vh, off);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKT[(16 * c + 8 * hh + e) * TP + 32 * w + l32] = Kr[c][e];
     }
@@ -430,7 +424,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
       int seen = r;
       if (!ATOMIC && r > 0 && tid == 0)  // poll early; checked after the first dQ block
         seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;
+      float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;  // uniform
 #pragma unroll
       for (int kc = 0; kc < NCOL; ++kc) {
 #pragma unroll 1
@@ -463,14 +457,17 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
           // (executed where such operations are coherent across XCDs); the
           // counters only serialise them, so each element receives the same
           // fp32 additions in the same order on every run.
+          const unsigned lane_off = 4u * (unsigned)((32 * mb + 4 * hh) * D + 32 * nb + l32);
+          if (!ATOMIC && r == 0) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = 32 * mb + 8 * (i / 4) + 4 * hh + (i % 4);
-            float* a = wsrow + (size_t)row * D + 32 * nb + l32;
-            if (!ATOMIC && r == 0)
-              __hip_atomic_exchange(a, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            else
-              __hip_atomic_fetch_add(a, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < 16; ++i)
+              __hip_atomic_exchange(at_bytes(wsrow, lane_off + 4u * ((8 * (i / 4) + (i % 4)) * D)), acc[i],
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              __hip_atomic_fetch_add(at_bytes(wsrow, lane_off + 4u * ((8 * (i / 4) + (i % 4)) * D)), acc[i],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }

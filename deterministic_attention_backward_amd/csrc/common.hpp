@@ -46,6 +46,17 @@ __device__ __forceinline__ bf16x8 cat44(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// base + a 32-bit byte offset: with a wave-uniform base this lets the compiler
+// use SGPR-base addressing instead of building a 64-bit address per lane.
+template <class T>
+__device__ __forceinline__ T* at_bytes(T* base, unsigned byte_off) {
+  return (T*)((char*)base + byte_off);
+}
+template <class T>
+__device__ __forceinline__ const T* at_bytes(const T* base, unsigned byte_off) {
+  return (const T*)((const char*)base + byte_off);
+}
+
 // Wait until every vector memory operation this wave issued has completed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
