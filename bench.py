@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--schedules", default="", help="comma list; default: every schedule valid for the mask")
     ap.add_argument("--no-nondet", action="store_true")
+    ap.add_argument("--dq-protocol", default="auto", choices=["auto", "device_atomic", "xcd_local"],
+                    help="dQ hand-off of the deterministic calls (auto picks XCD-local where it applies)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle leg (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
@@ -143,6 +145,7 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible: the benchmark needs an MI355X")
     lib = _lib.load()
+    dab.set_dq_protocol(args.dq_protocol)
     events = HipEvents()
     w = attn_inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.describe()} seed={w.seed}")
@@ -203,6 +206,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.describe()}", "schedule": best, "tile": T, "n_tiles": N,
+                   "dq_protocol": args.dq_protocol,
                    "seed": w.seed, "flops_per_step": w.flops},
         "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
         "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,

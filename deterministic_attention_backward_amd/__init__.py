@@ -171,6 +171,14 @@ def schedule_plan(n_tiles: int, causal: bool, schedule):
     return n_workers, recs
 
 
+DQ_PROTOCOLS = {"auto": 0, "device_atomic": 1, "xcd_local": 2}
+
+
+def set_dq_protocol(protocol="auto") -> None:
+    """Debug: force the dQ hand-off protocol of deterministic calls ("auto", "device_atomic", "xcd_local")."""
+    _lib.check(_lib.load().attn_debug_set_dq_protocol(DQ_PROTOCOLS[protocol]), "attn_debug_set_dq_protocol")
+
+
 def set_wait_limit(iterations: int = 0, poison: bool = False) -> None:
     """Debug: bound on one dQ ordering wait (0 = default) and counter poisoning for the next calls."""
     _lib.load().attn_debug_set_wait_limit(int(iterations), 1 if poison else 0)

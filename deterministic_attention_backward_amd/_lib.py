@@ -34,6 +34,7 @@ EXPORTS = (
     "attn_schedule_plan",
     "attn_debug_set_wait_limit",
     "attn_set_timing_events",
+    "attn_debug_set_dq_protocol",
 )
 
 _lib = None
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.attn_debug_set_wait_limit.restype = None
     lib.attn_set_timing_events.argtypes = [vp, vp]
     lib.attn_set_timing_events.restype = None
+    lib.attn_debug_set_dq_protocol.argtypes = [i]
+    lib.attn_debug_set_dq_protocol.restype = i
     _lib = lib
     return lib
 

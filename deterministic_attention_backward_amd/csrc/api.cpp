@@ -17,6 +17,7 @@ namespace {
 constexpr uint32_t kDefaultWaitLimit = 1u << 24;
 uint32_t g_wait_limit = kDefaultWaitLimit;
 int g_poison = 0;
+int g_dq_protocol = DQ_AUTO;
 hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 constexpr int kMaxDevices = 64;
@@ -113,6 +114,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   a.atomic = deterministic ? 0 : 1;
   a.wait_limit = g_wait_limit;
   a.poison = g_poison;
+  a.dq_protocol = g_dq_protocol;
   a.ev_before = g_ev_before;
   a.ev_after = g_ev_after;
   const hipError_t e = launch_bwd(a, num_cu, static_cast<hipStream_t>(stream));
@@ -237,6 +239,12 @@ void attn_set_timing_events(void* before, void* after) {
   } else {
     g_ev_before = g_ev_after = nullptr;
   }
+}
+
+int attn_debug_set_dq_protocol(int protocol) {
+  if (protocol < DQ_AUTO || protocol > DQ_XCD_LOCAL) return ATTN_ERR_INVALID_ARG;
+  g_dq_protocol = protocol;
+  return ATTN_OK;
 }
 
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter) {

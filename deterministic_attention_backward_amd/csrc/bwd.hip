@@ -28,7 +28,8 @@ struct PreParams {
   const bf16 *o, *dout;
   const float* lse;
   float *lse2, *delta, *dq_ws;
-  int *counters, *header;
+  int *counters, *header, *heads;
+  long long n_heads;    // entries of the head table
   long long rows;       // BH * S_pad
   int S, S_pad;
   long long n_counters;
@@ -66,6 +67,7 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
   for (long long i = gtid; i < p.n_counters; i += nthreads)
     p.counters[i] = (p.poison && i == p.n_counters - 1) ? 0x40000000 : 0;
   if (gtid < 64) p.header[gtid] = 0;
+  for (long long i = gtid; i < p.n_heads; i += nthreads) p.heads[i] = -1;
   for (long long i = gtid * 4; i < p.dq_ws_elems; i += nthreads * 4)
     *(f32x4*)(p.dq_ws + i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
@@ -90,8 +92,9 @@ struct MainParams {
   bf16 *dk, *dv;
   const float *lse2, *delta;
   float *dq_ws, *park;
-  int *counters, *header;
-  int S, S_pad, N, n_qsub, n_workers, n_units, sched;
+  bf16* dq;
+  int *counters, *header, *heads;
+  int S, S_pad, N, n_qsub, n_workers, n_units, sched, BH;
   float scale, scale_log2;
   uint32_t wait_limit;
 };
@@ -111,8 +114,17 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
 // quads of each 16-query group in transposed LDS rows are stored in the order 0, 2, 1, 3
 __device__ __forceinline__ int quad_pos(int qg) { return 16 * (qg >> 2) + 4 * ((qg & 1) * 2 + ((qg >> 1) & 1)); }
 
-template <int D, int T, int BR, bool CAUSAL, bool ATOMIC>
+// How a unit hands its dQ partials over.
+enum {
+  MODE_ATOMIC = 0,  // non-deterministic: fp32 atomic adds in whatever order they land
+  MODE_DEVICE = 1,  // deterministic: device-scope atomic RMWs serialised by the counters
+  MODE_XCD = 2      // deterministic: all workers of a head on one XCD, plain RMW via its L2
+};
+
+template <int D, int T, int BR, bool CAUSAL, int MODE>
 __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) {
+  constexpr bool ATOMIC = MODE == MODE_ATOMIC;
+  constexpr bool XCD = MODE == MODE_XCD;
   constexpr int NW = T / 32;
   constexpr int NT = NW * 64;
   constexpr int DP = D + 8;        // row-major Q/dO rows (bf16 elements)
@@ -139,7 +151,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
   __shared__ __attribute__((aligned(16))) bf16 sdST[T * SP];
   __shared__ __attribute__((aligned(16))) float sL[BR];
   __shared__ __attribute__((aligned(16))) float sDl[BR];
-  __shared__ int sUnit;
+  __shared__ int sUnit[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,7 +161,11 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
   const int S = p.S;
 
   bf16x8 Kr[KC], Vr[KC];           // B operands of S and dP (this wave's keys)
-  bf16x8 Kd[NCOL][TC];             // B operand of dQ (all keys, this wave's columns)
+  // B operand of dQ (all keys, this wave's columns): registers, except in the
+  // XCD-local mode, which needs those registers for the in-flight running sums
+  // and reads the operand from the K^T tile in LDS instead.
+  constexpr bool KD_REG = !XCD;
+  bf16x8 Kd[KD_REG ? NCOL : 1][KD_REG ? TC : 1];
   f32x16 dKa[ND], dVa[ND];
   u32x4 stq[GPT][4], sto[GPT][4];  // staged next sub-tile
   float stl = 0.0f, std_ = 0.0f;
@@ -225,11 +241,13 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
       for (int e = 0; e < 8; ++e) sKT[(16 * c + 8 * hh + e) * TP + 32 * w + l32] = Kr[c][e];
     }
     __syncthreads();
+    if (KD_REG) {
 #pragma unroll
-    for (int kc = 0; kc < NCOL; ++kc) {
+      for (int kc = 0; kc < NCOL; ++kc) {
 #pragma unroll
-      for (int c = 0; c < TC; ++c)
-        Kd[kc][c] = *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
+        for (int c = 0; c < TC; ++c)
+          Kd[KD_REG ? kc : 0][KD_REG ? c : 0] = *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
+      }
     }
   };
 
@@ -269,14 +287,53 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
     wait_vmem();
   };
 
+  int xq = 0;  // this workgroup's XCD, the queue it takes units from
+  if (XCD) {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    xq = (int)(x & (kMaxQueues - 1));
+  }
+
   for (;;) {
     __syncthreads();
-    if (tid == 0) sUnit = atomicAdd(&p.header[0], 1);
+    if (tid == 0) {
+      if (!XCD) {
+        const int u = atomicAdd(&p.header[0], 1);
+        sUnit[0] = u < p.n_units ? u / p.n_workers : p.BH;
+        sUnit[1] = u % p.n_workers;
+      } else {
+        // Units of one head are consecutive tickets of one XCD's queue; the
+        // ticket of a head's first worker claims the next unclaimed head and
+        // publishes it for the others (lower tickets are held by running
+        // workgroups, so the wait below always ends).
+        const int k = atomicAdd(&p.header[16 + xq], 1);
+        const int i = k / p.n_workers, wk = k % p.n_workers;
+        int head = p.BH;
+        if (i < p.BH) {
+          int* slot = &p.heads[xq * p.BH + i];
+          if (wk == 0) {
+            head = min(atomicAdd(&p.header[2], 1), p.BH);
+            __hip_atomic_store(slot, head, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            uint32_t it = 0;
+            while ((head = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < 0) {
+              if (++it >= p.wait_limit) {
+                __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                head = p.BH;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+          }
+        }
+        sUnit[0] = head;
+        sUnit[1] = wk;
+      }
+    }
     __syncthreads();
-    const int unit = sUnit;
-    if (unit >= p.n_units) break;
-    const int bh = unit / p.n_workers;
-    const int wk = unit % p.n_workers;
+    const int bh = sUnit[0];
+    const int wk = sUnit[1];
+    if (bh >= p.BH) break;
     const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
     const int total = ntasks * NSUB;
 
@@ -411,7 +468,7 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
       pend = -1;
       if (idx + 1 < total) {
         stage_store();
-        if (idx + 2 < total) {
+        if (!XCD && idx + 2 < total) {  // prefetch now: it lands during the dQ phase and the next S/dP
           const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, (idx + 2) / NSUB);
           stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
         }
@@ -422,56 +479,101 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
       const int r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, qi, kj);
       const bool last = ATOMIC ? true : (r == sched_contributors(p.N, CAUSAL, qi) - 1);
       int seen = r;
-      if (!ATOMIC && r > 0 && tid == 0)  // poll early; checked after the first dQ block
+      if (!ATOMIC && r > 0 && tid == 0)  // poll early
         seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;  // uniform
-#pragma unroll
-      for (int kc = 0; kc < NCOL; ++kc) {
-#pragma unroll 1
-        for (int kr = 0; kr < NROW; ++kr) {
-          const int nb = col_of(kc), mb = row_of(kr);
-          f32x16 acc = zero16();
-          const int grp = lane >> 4, gi = lane & 15;
-          const bf16* base = &sdST[(8 * (grp >> 1) + (gi >> 2)) * SP + 32 * mb + 16 * (grp & 1) + 4 * (gi & 3)];
-#pragma unroll
-          for (int c = 0; c < TC; ++c) {
-            const bf16x8 a = cat44(lds_read_tr(base + 16 * c * SP), lds_read_tr(base + (16 * c + 4) * SP));
-            acc = mfma32(a, Kd[kc][c], acc);
-          }
-          if (!ATOMIC && r > 0 && kc == 0 && kr == 0) {
-            // Turn-taking: wait until the previous contributor's RMWs are done.
-            if (tid == 0) {
-              uint32_t it = 0;
-              while (seen != r) {
-                if (++it >= p.wait_limit) {
-                  __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                  break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-                seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
+
+      // Turn-taking: wait until the previous contributor's update is complete.
+      auto wait_turn = [&]() {
+        if (tid == 0) {
+          uint32_t it = 0;
+          while (seen != r) {
+            if (++it >= p.wait_limit) {
+              __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
             }
-            __syncthreads();
+            __builtin_amdgcn_s_sleep(2);
+            seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          // Every access to the dQ accumulator is a device-scope atomic RMW
-          // (executed where such operations are coherent across XCDs); the
-          // counters only serialise them, so each element receives the same
-          // fp32 additions in the same order on every run.
-          const unsigned lane_off = 4u * (unsigned)((32 * mb + 4 * hh) * D + 32 * nb + l32);
-          if (!ATOMIC && r == 0) {
+        }
+        __syncthreads();
+      };
+      auto dq_block = [&](int kc, int mb) {
+        f32x16 acc = zero16();
+        const int grp = lane >> 4, gi = lane & 15;
+        const bf16* base = &sdST[(8 * (grp >> 1) + (gi >> 2)) * SP + 32 * mb + 16 * (grp & 1) + 4 * (gi & 3)];
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              __hip_atomic_exchange(at_bytes(wsrow, lane_off + 4u * ((8 * (i / 4) + (i % 4)) * D)), acc[i],
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
+        for (int c = 0; c < TC; ++c) {
+          const bf16x8 a = cat44(lds_read_tr(base + 16 * c * SP), lds_read_tr(base + (16 * c + 4) * SP));
+          const bf16x8 kb = KD_REG ? Kd[KD_REG ? kc : 0][KD_REG ? c : 0]
+                                   : *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
+          acc = mfma32(a, kb, acc);
+        }
+        return acc;
+      };
+      auto elem_off = [&](int nb, int mb, int i) {
+        return 4u * (unsigned)((32 * mb + 4 * hh + 8 * (i / 4) + (i % 4)) * D + 32 * nb + l32);
+      };
+
+      if (XCD) {
+        // Every contributor of this tile runs on this XCD, so its L2 holds the
+        // accumulator coherently for all of them. After our turn, drop this
+        // CU's write-through L1 copies, start the loads of the running sum,
+        // compute the partial while they are in flight, then add and store.
+        // (The first contributor adds to 0, which only turns -0 into +0.)
+        static_assert(!XCD || NCOL * NROW == 2, "XCD-local hand-off is written for two dQ blocks per wave");
+        const int nb0 = col_of(0), mb0 = row_of(0);
+        const int nb1 = col_of(NCOL > 1 ? 1 : 0), mb1 = row_of(NCOL > 1 ? 0 : 1);
+        const f32x16 acc0 = dq_block(0, mb0);  // overlaps the early poll
+        float prev0[16], prev1[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              __hip_atomic_fetch_add(at_bytes(wsrow, lane_off + 4u * ((8 * (i / 4) + (i % 4)) * D)), acc[i],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < 16; ++i) prev0[i] = prev1[i] = 0.0f;
+        if (r > 0) {
+          wait_turn();
+          asm volatile("buffer_inv sc0" ::: "memory");
+#pragma unroll
+          for (int i = 0; i < 16; ++i) prev0[i] = *at_bytes(wsrow, elem_off(nb0, mb0, i));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) prev1[i] = *at_bytes(wsrow, elem_off(nb1, mb1, i));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the second block's MFMAs
+        const f32x16 acc1 = dq_block(NCOL > 1 ? 1 : 0, mb1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *at_bytes(wsrow, elem_off(nb0, mb0, i)) = prev0[i] + acc0[i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *at_bytes(wsrow, elem_off(nb1, mb1, i)) = prev1[i] + acc1[i];
+      } else {
+        // Device-scope atomic RMWs (the deterministic mode serialises them with
+        // the counters, so each element receives the same fp32 additions in
+        // the same order on every run; the first contributor swaps its value in).
+#pragma unroll
+        for (int kc = 0; kc < NCOL; ++kc) {
+#pragma unroll 1
+          for (int kr = 0; kr < NROW; ++kr) {
+            const int nb = col_of(kc), mb = row_of(kr);
+            const f32x16 acc = dq_block(kc, mb);
+            if (!ATOMIC && r > 0 && kc == 0 && kr == 0) wait_turn();
+            if (!ATOMIC && r == 0) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                __hip_atomic_exchange(at_bytes(wsrow, elem_off(nb, mb, i)), acc[i], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                __hip_atomic_fetch_add(at_bytes(wsrow, elem_off(nb, mb, i)), acc[i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
       if (!ATOMIC && !last) pend = cidx;
+      // XCD-local mode prefetches here, keeping the dQ phase free of staging
+      // registers; the loads still have the whole next S/dP phase to land
+      if (XCD && idx + 2 < total) {
+        const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, (idx + 2) / NSUB);
+        stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
+      }
     }
     if (pend >= 0) {  // the unit's last hand-off
       wait_vmem();
@@ -507,11 +609,19 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
 // --------------------------------------------------------------------------------------
 // launcher
 
-template <int D, int T, int BR, bool CAUSAL, bool ATOMIC>
-static hipError_t launch_main(const MainParams& mp, int num_cu, hipStream_t stream, int* grid_out) {
-  auto kern = bwd_main_kernel<D, T, BR, CAUSAL, ATOMIC>;
+template <int D, int T, int BR, bool CAUSAL, int MODE>
+static hipError_t launch_main(const MainParams& mp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_main_kernel<D, T, BR, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T / 32 * 64), 0, stream,
+                     mp);
+  return hipGetLastError();
+}
+
+template <int D, int T, int BR, bool CAUSAL>
+static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int protocol, hipStream_t stream,
+                              int* xcd_out) {
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, T / 32 * 64, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, bwd_main_kernel<D, T, BR, CAUSAL, MODE_DEVICE>, T / 32 * 64, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long long grid = (long long)num_cu * per_cu;
@@ -519,22 +629,29 @@ static hipError_t launch_main(const MainParams& mp, int num_cu, hipStream_t stre
   if (grid > mp.n_units) grid = mp.n_units;
   // Cyclic dQ waits (Shift, Symmetric Shift) need every worker of a head
   // resident at once; the persistent grid must hold at least one head.
-  if (!ATOMIC && (mp.sched == SCHED_SHIFT || mp.sched == SCHED_SYMMETRIC_SHIFT) && grid < mp.n_workers)
-    return hipErrorInvalidConfiguration;
-  *grid_out = (int)grid;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(T / 32 * 64), 0, stream, mp);
-  return hipGetLastError();
+  const bool cyclic = mp.sched == SCHED_SHIFT || mp.sched == SCHED_SYMMETRIC_SHIFT;
+  if (!atomic && cyclic && grid < mp.n_workers) return hipErrorInvalidConfiguration;
+  // XCD-local hand-off: workgroup g runs on XCD g % 8 (gfx950, 8 XCDs per
+  // device in SPX mode), so each XCD holds grid / 8 of the persistent
+  // workgroups. Cyclic schedules need all workers of a head resident there.
+  const int n_xcd = (num_cu >= 64 && num_cu % 8 == 0) ? 8 : 1;
+  const long long per_xcd = grid / n_xcd;
+  // (the XCD-local hand-off is written for two dQ blocks per wave)
+  constexpr bool kXcdShape = (BR / 32) * (D / 32) == 2 * (T / 32);
+  const bool xcd = kXcdShape && !atomic && protocol != DQ_DEVICE_ATOMIC && (!cyclic || mp.n_workers <= per_xcd);
+  *xcd_out = xcd ? 1 : 0;
+  if (atomic) return launch_main<D, T, BR, CAUSAL, MODE_ATOMIC>(mp, (int)grid, stream);
+  if constexpr (kXcdShape) {
+    if (xcd) return launch_main<D, T, BR, CAUSAL, MODE_XCD>(mp, (int)grid, stream);
+  }
+  return launch_main<D, T, BR, CAUSAL, MODE_DEVICE>(mp, (int)grid, stream);
 }
 
 template <int D, int T, int BR>
-static hipError_t dispatch_mask(const MainParams& mp, bool causal, bool atomic, int num_cu, hipStream_t s,
-                                int* grid) {
-  if (causal) {
-    return atomic ? launch_main<D, T, BR, true, true>(mp, num_cu, s, grid)
-                  : launch_main<D, T, BR, true, false>(mp, num_cu, s, grid);
-  }
-  return atomic ? launch_main<D, T, BR, false, true>(mp, num_cu, s, grid)
-                : launch_main<D, T, BR, false, false>(mp, num_cu, s, grid);
+static hipError_t dispatch_mask(const MainParams& mp, bool causal, bool atomic, int num_cu, int protocol,
+                                hipStream_t s, int* xcd) {
+  return causal ? launch_mask<D, T, BR, true>(mp, atomic, num_cu, protocol, s, xcd)
+                : launch_mask<D, T, BR, false>(mp, atomic, num_cu, protocol, s, xcd);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
@@ -545,6 +662,7 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   float* delta = (float*)(a.ws + a.lay.delta);
   float* dq_ws = (float*)(a.ws + a.lay.dq_ws);
   float* park = (float*)(a.ws + a.lay.park);
+  int* heads = (int*)(a.ws + a.lay.heads);
 
   PreParams pp;
   pp.o = (const bf16*)a.o;
@@ -555,6 +673,8 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   pp.dq_ws = dq_ws;
   pp.counters = counters;
   pp.header = header;
+  pp.heads = heads;
+  pp.n_heads = (long long)kMaxQueues * BH;
   pp.rows = BH * a.S_pad;
   pp.S = a.S;
   pp.S_pad = a.S_pad;
@@ -583,6 +703,9 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.park = park;
   mp.counters = counters;
   mp.header = header;
+  mp.heads = heads;
+  mp.dq = (bf16*)a.dq;
+  mp.BH = (int)BH;
   mp.S = a.S;
   mp.S_pad = a.S_pad;
   mp.N = a.N;
@@ -594,17 +717,17 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.scale_log2 = a.scale * 1.4426950408889634f;
   mp.wait_limit = a.wait_limit;
 
-  int grid = 0;
+  int xcd_local = 0;
   hipError_t e = hipErrorInvalidValue;
   const bool causal = a.causal != 0, atomic = a.atomic != 0;
   if (a.ev_before && a.ev_after) {
     e = hipEventRecord(a.ev_before, stream);
     if (e != hipSuccess) return e;
   }
-  if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, stream, &grid);
-  else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
-  else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, stream, &grid);
-  else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, stream, &grid);
+  if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
+  else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
+  else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
+  else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
   if (e != hipSuccess) return e;
   if (a.ev_before && a.ev_after) {
     e = hipEventRecord(a.ev_after, stream);

@@ -11,10 +11,18 @@ namespace attn {
 // persistent grid never exceeds this.
 constexpr int kMaxGrid = 512;
 
+// Unit queues for XCD-local placement: one per XCD id (gfx950 reports 0..7).
+constexpr int kMaxQueues = 16;
+
+// dQ hand-off protocols (attn_debug_set_dq_protocol)
+enum { DQ_AUTO = 0, DQ_DEVICE_ATOMIC = 1, DQ_XCD_LOCAL = 2 };
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte layout of the backward workspace (every region 256-byte aligned):
-//   header   int32[64]: [0] unit ticket, [1] timeout flag
+//   header   int32[64]: [0] unit ticket, [1] timeout flag, [2] next head to
+//            claim, [16 + q] unit ticket of XCD queue q
+//   heads    int32[kMaxQueues * BH]: head claimed by each local head slot of a queue
 //   counters int32[BH * n_qsub]: per (head, query sub-tile) dQ turn counter
 //   lse2     fp32[BH * S_pad]: lse * log2(e), +inf on padding rows
 //   delta    fp32[BH * S_pad]: rowsum(dO * O), 0 on padding rows
@@ -22,13 +30,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //   park     fp32[kMaxGrid * 2 * T * D * 2]: Symmetric Shift only; per workgroup,
 //            one slot per KV tile of its pair, each holding dK and dV
 struct WsLayout {
-  size_t header, counters, lse2, delta, dq_ws, park, total;
+  size_t header, heads, counters, lse2, delta, dq_ws, park, total;
 };
 
 inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, bool park) {
   WsLayout w;
   size_t off = 0;
   w.header = off;   off += align256(64 * sizeof(int));
+  w.heads = off;    off += align256(size_t(kMaxQueues) * BH * sizeof(int));
   w.counters = off; off += align256(size_t(BH) * n_qsub * sizeof(int));
   w.lse2 = off;     off += align256(size_t(BH) * S_pad * sizeof(float));
   w.delta = off;    off += align256(size_t(BH) * S_pad * sizeof(float));
@@ -49,6 +58,7 @@ struct BwdArgs {
   int causal, sched, atomic;
   uint32_t wait_limit;
   int poison;
+  int dq_protocol;                 // DQ_AUTO / DQ_DEVICE_ATOMIC / DQ_XCD_LOCAL
   hipEvent_t ev_before, ev_after;  // optional: recorded around the main kernel
 };
 

@@ -160,6 +160,21 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
 
 /*
+ * attn_debug_set_dq_protocol - how deterministic calls hand dQ partials over
+ * (the order is the schedule's in every case):
+ *   0 (default) choose per call: XCD-local when every worker of a head can be
+ *     resident on one XCD (always for NAIVE/DESCENDING; for SHIFT and
+ *     SYMMETRIC_SHIFT when the workers per head fit the XCD), else 1;
+ *   1 device-scope atomic read-modify-writes, serialised by the counters;
+ *   2 XCD-local: all workers of a head run on one XCD and update the fp32
+ *     accumulator with plain loads/stores through that XCD's L2 (falls back
+ *     to 1 where the workers of a head would not be co-resident).
+ * Returns ATTN_ERR_INVALID_ARG for other values. Process-wide, not
+ * thread-safe; for tests and measurements.
+ */
+int attn_debug_set_dq_protocol(int protocol);
+
+/*
  * attn_set_timing_events - profiling hook. When both arguments are non-NULL
  * hipEvent_t handles (created by the caller), every following backward call
  * records `before` on its stream immediately before launching its main tile

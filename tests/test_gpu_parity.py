@@ -115,15 +115,20 @@ def test_forward_parity(case):
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dS%dD%d%s_t%d" % (c[0], c[1], c[2], c[3],
                                                                               "c" if c[4] else "f", c[6]))
-def test_backward_parity(case):
+@pytest.mark.parametrize("protocol", ["auto", "device_atomic"])
+def test_backward_parity(case, protocol):
     B, H, S, D, causal, seed, tile = case
     c = Case(B, H, S, D, causal, seed)
     dq_r, dk_r, dv_r = c.ref()
-    for sched in schedules_for(S, D, causal, tile):
-        say(f"backward parity {case} schedule={sched or 'atomic'}")
-        dq, dk, dv = c.run(sched, tile)
-        for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
-            assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
+    try:
+        dab.set_dq_protocol(protocol)
+        for sched in schedules_for(S, D, causal, tile):
+            say(f"backward parity {case} schedule={sched or 'atomic'} dq protocol={protocol}")
+            dq, dk, dv = c.run(sched, tile)
+            for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+                assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
+    finally:
+        dab.set_dq_protocol("auto")
 
 
 DET_CASES = [
@@ -135,20 +140,25 @@ DET_CASES = [
 
 @pytest.mark.parametrize("case", DET_CASES, ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3],
                                                                               "c" if c[4] else "f"))
-def test_bitwise_reproducible_20_runs(case):
+@pytest.mark.parametrize("protocol", ["auto", "device_atomic"])
+def test_bitwise_reproducible_20_runs(case, protocol):
     B, H, S, D, causal, seed = case
     c = Case(B, H, S, D, causal, seed)
-    for sched in schedules_for(S, D, causal, 0)[:-1]:
-        say(f"determinism {case} schedule={sched}")
-        digests = set()
-        for _ in range(20):
-            out = tuple(torch.full_like(c.q, float("nan")) for _ in range(3))
-            dq, dk, dv = c.run(sched, 0, out=out)
-            h = hashlib.sha256()
-            for t in (dq, dk, dv):
-                h.update(t.view(torch.int16).cpu().numpy().tobytes())
-            digests.add(h.hexdigest())
-        assert len(digests) == 1, f"{sched}: {len(digests)} distinct results in 20 runs"
+    try:
+        dab.set_dq_protocol(protocol)
+        for sched in schedules_for(S, D, causal, 0)[:-1]:
+            say(f"determinism {case} schedule={sched} dq protocol={protocol}")
+            digests = set()
+            for _ in range(20):
+                out = tuple(torch.full_like(c.q, float("nan")) for _ in range(3))
+                dq, dk, dv = c.run(sched, 0, out=out)
+                h = hashlib.sha256()
+                for t in (dq, dk, dv):
+                    h.update(t.view(torch.int16).cpu().numpy().tobytes())
+                digests.add(h.hexdigest())
+            assert len(digests) == 1, f"{sched}: {len(digests)} distinct results in 20 runs"
+    finally:
+        dab.set_dq_protocol("auto")
 
 
 def test_forward_bitwise_reproducible():
