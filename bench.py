@@ -85,6 +85,32 @@ def time_variant(fn, steps, warmup, torch, events, lib):
     return wall / steps * 1e3, sum(kern) / len(kern)
 
 
+KERNEL_SOURCES = ("bwd.hip", "common.hpp", "schedule.hpp", "launch.hpp")
+
+
+def measured_traffic(workload: str, schedule: str, protocol: str):
+    """HBM bytes per launch of the main kernel from the committed counter record.
+
+    profiles/bwd_main_C2_traffic.json holds FETCH_SIZE + WRITE_SIZE (scaled by
+    a 1 GiB copy) for one workload/schedule, with a hash of the kernel sources it
+    was taken on. Returns None unless it matches this run and the sources are
+    unchanged since.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "bwd_main_C2_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "deterministic_attention_backward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if (rec.get("kernel_source_sha256") != h.hexdigest() or not rec.get("workload", "").startswith(workload + ":")
+            or rec.get("schedule") != schedule or rec.get("dq_protocol") != protocol):
+        return None
+    return float(rec["traffic_bytes"])
+
+
 def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
     """The float64 oracle backward on whole heads of the same workload, time-bounded."""
     import numpy as np
@@ -214,7 +240,9 @@ def main():
                           "tflops": round(v["tflops"], 2)} for s, v in results.items()},
         "nondet": {k2: round(v2, 4) for k2, v2 in nondet.items()} if nondet else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, best, args.dq_protocol),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "kernel": "bwd_main_kernel", "kernel_ms": round(r["kernel_ms"], 4)},
     }
     if args.cpu_seconds > 0:
