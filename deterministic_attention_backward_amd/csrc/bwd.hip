@@ -75,16 +75,22 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
 // --------------------------------------------------------------------------------------
 // main kernel
 //
-// Workgroup = T/32 waves; wave w owns keys 32w..32w+31 of the current KV tile.
-// Registers hold, for the whole unit: this wave's K and V rows as the B
-// operands of S = Q K^T and dP = dO V^T, the K columns it needs as the B
-// operand of dQ = dS K, and the dK/dV accumulators. Per query sub-tile
-// (BR rows) LDS holds Q and dO twice: row-major (A operands of S and dP) and
-// transposed with the queries of every 16-row group permuted so that one
-// 16-byte read yields a lane's eight k-values of the dV/dK B operand in the
-// order the P/dS accumulators supply them. dS goes to LDS transposed (one
-// 8-byte write per accumulator quad) and comes back through the gfx950
-// transpose read as the A operand of dQ.
+// A workgroup holds one KV tile of T keys and runs two kinds of waves, one of
+// each per SIMD:
+//   tile waves (T/32): wave a owns keys 32a..32a+31. Its registers hold those
+//     keys' K and V rows (B operands of S = Q K^T and dP = dO V^T) and their dK
+//     and dV accumulators for the whole run of tasks on the tile. Per query
+//     sub-tile of BR rows it computes S, dP, P and dS, writes dS^T to LDS and
+//     accumulates dV += P^T dO and dK += dS^T Q.
+//   dQ waves (T/32): stage the query sub-tiles (Q, dO, LSE, Delta) from HBM into
+//     LDS and, one sub-tile behind the tile waves, compute dQ = dS K from the
+//     dS^T the tile waves left in LDS (K columns held in registers) and hand the
+//     partial over to the fp32 dQ workspace in the schedule's order.
+// Two workgroup barriers per sub-tile order the hand-over between the roles
+// (X: the dQ waves are done with the previous dS^T and have written this
+// sub-tile's transposed Q/dO; Y: the tile waves are done with the sub-tile).
+// Row-major Q/dO are double-buffered; the transposed copies and dS^T are
+// single-buffered and protected by those two barriers.
 
 struct MainParams {
   const bf16 *q, *k, *v;
@@ -99,8 +105,6 @@ struct MainParams {
   uint32_t wait_limit;
 };
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
 // Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // supplies the address of a 4-element row chunk and receives element i % 4 of
 // the chunks supplied by lanes 4e + i / 4, e = 0..3.
@@ -114,6 +118,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
 // quads of each 16-query group in transposed LDS rows are stored in the order 0, 2, 1, 3
 __device__ __forceinline__ int quad_pos(int qg) { return 16 * (qg >> 2) + 4 * ((qg & 1) * 2 + ((qg >> 1) & 1)); }
 
+// Workgroup barrier over LDS only: this wave's LDS operations complete
+// (lgkmcnt(0)) before it arrives; its global loads and stores stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // How a unit hands its dQ partials over.
 enum {
   MODE_ATOMIC = 0,  // non-deterministic: fp32 atomic adds in whatever order they land
@@ -121,66 +134,320 @@ enum {
   MODE_XCD = 2      // deterministic: all workers of a head on one XCD, plain RMW via its L2
 };
 
-template <int D, int T, int BR, bool CAUSAL, int MODE>
-__global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) {
-  constexpr bool ATOMIC = MODE == MODE_ATOMIC;
-  constexpr bool XCD = MODE == MODE_XCD;
-  constexpr int NW = T / 32;
-  constexpr int NT = NW * 64;
-  constexpr int DP = D + 8;        // row-major Q/dO rows (bf16 elements)
-  constexpr int BRP = BR + 8;      // transposed Q/dO rows
-  constexpr int TP = T + 8;        // transposed K rows
-  constexpr int SP = BR + 4;       // transposed dS rows
-  constexpr int KC = D / 16;       // k-chunks over the feature dimension
-  constexpr int ND = D / 32;       // 32-wide feature blocks
-  constexpr int MB = BR / 32;      // 32-row query blocks per sub-tile
-  constexpr int NSUB = T / BR;     // query sub-tiles per task
-  constexpr int QBW = MB * ND / NW;             // dQ 32x32 blocks per wave
-  constexpr int NCOL = ND >= NW ? ND / NW : 1;  // ... in this many feature columns
-  constexpr int NROW = QBW / NCOL;              // ... and this many query rows
-  constexpr int TC = T / 16;       // k-chunks over the keys
-  constexpr int GROUPS = (BR / 4) * (D / 8);  // staging pieces: 4 rows x 8 features
-  constexpr int GPT = GROUPS / NT;
-  static_assert(QBW * NW == MB * ND && GROUPS % NT == 0 && T % BR == 0, "tile shape");
+template <int D_, int T_, int BR_>
+struct Geo {
+  static constexpr int D = D_, T = T_, BR = BR_;
+  static constexpr int NA = T / 32;            // tile waves
+  static constexpr int NB = NA;                // dQ waves
+  static constexpr int NTA = NA * 64, NTB = NB * 64, NT = NTA + NTB;
+  static constexpr int DP = D + 8;             // row-major Q/dO rows (bf16 elements)
+  static constexpr int BRP = BR + 8;           // transposed Q/dO rows
+  static constexpr int TP = T + 8;             // transposed K rows
+  static constexpr int SP = BR + 4;            // transposed dS rows
+  static constexpr int KC = D / 16;            // k-chunks over the features
+  static constexpr int ND = D / 32;            // 32-wide feature blocks
+  static constexpr int MB = BR / 32;           // 32-row query blocks per sub-tile
+  static constexpr int NSUB = T / BR;          // sub-tiles per task
+  static constexpr int TC = T / 16;            // k-chunks over the keys
+  static constexpr int QBW = MB * ND / NB;     // dQ blocks per dQ wave: one row block, QBW feature blocks
+  static constexpr int GROUPS = (BR / 4) * (D / 8);  // staging pieces: 4 rows x 8 features
+  static constexpr int GPT = GROUPS / NTB;
+  // LDS regions (bytes)
+  static constexpr int RM_BYTES = 2 * BR * DP * 2 + 2 * BR * 4;  // one row-major buffer: Q, dO, LSE, Delta
+  static constexpr int TR_OFF = 2 * RM_BYTES;
+  static constexpr int TR_BYTES = 2 * D * BRP * 2;               // Q^T, dO^T (K^T at a tile start)
+  static constexpr int DS_OFF = TR_OFF + TR_BYTES;
+  static constexpr int DS_BYTES = T * SP * 2;
+  // D = 128: the tile waves keep V in LDS (row-major, each wave reads only the
+  // rows it wrote) so that K, dK and dV fit their registers without spilling
+  static constexpr bool V_LDS = D >= 128;
+  static constexpr int SV_OFF = DS_OFF + DS_BYTES;
+  static constexpr int SV_BYTES = V_LDS ? T * DP * 2 : 0;
+  static constexpr int UNIT_OFF = SV_OFF + SV_BYTES;
+  static constexpr int LDS_BYTES = UNIT_OFF + 16;
+  static_assert(QBW >= 1 && QBW * NB == MB * ND && QBW <= ND && ND % QBW == 0, "dQ block split");
+  static_assert(GPT >= 1 && GROUPS % NTB == 0 && T % BR == 0 && BR <= NTB, "staging split");
+  static_assert(D * TP * 2 <= TR_BYTES, "K^T must fit the transposed staging area");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[BR * DP];
-  __shared__ __attribute__((aligned(16))) bf16 sO[BR * DP];
-  __shared__ __attribute__((aligned(16))) bf16 sQT[D * BRP];
-  __shared__ __attribute__((aligned(16))) bf16 sOT[D * BRP];
-  __shared__ __attribute__((aligned(16))) bf16 sKT[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 sdST[T * SP];
-  __shared__ __attribute__((aligned(16))) float sL[BR];
-  __shared__ __attribute__((aligned(16))) float sDl[BR];
-  __shared__ int sUnit[2];
+template <class G>
+struct Lds {
+  char* base;
+  __device__ __forceinline__ bf16* q(int b) const { return (bf16*)(base + b * G::RM_BYTES); }
+  __device__ __forceinline__ bf16* o(int b) const { return q(b) + G::BR * G::DP; }
+  __device__ __forceinline__ float* lse(int b) const { return (float*)(base + b * G::RM_BYTES + 2 * G::BR * G::DP * 2); }
+  __device__ __forceinline__ float* dl(int b) const { return lse(b) + G::BR; }
+  __device__ __forceinline__ bf16* qt() const { return (bf16*)(base + G::TR_OFF); }
+  __device__ __forceinline__ bf16* ot() const { return qt() + G::D * G::BRP; }
+  __device__ __forceinline__ bf16* kt() const { return qt(); }
+  __device__ __forceinline__ bf16* dst() const { return (bf16*)(base + G::DS_OFF); }
+  __device__ __forceinline__ bf16* v() const { return (bf16*)(base + G::SV_OFF); }
+  __device__ __forceinline__ int* unit() const { return (int*)(base + G::UNIT_OFF); }
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-  const int S = p.S;
+// A run of consecutive tasks of one unit on the same KV tile (wave-uniform).
+struct Seg {
+  int bh, wk, t0, n;  // head, worker, first task, sub-tiles in the run
+  int kv, slot;       // KV tile and its parking slot
+  bool restore;       // accumulators parked earlier in this unit: reload them
+  bool keep;          // the tile comes back later in this unit: park at the end
+};
 
-  bf16x8 Kr[KC], Vr[KC];           // B operands of S and dP (this wave's keys)
-  // B operand of dQ (all keys, this wave's columns): registers, except in the
-  // XCD-local mode, which needs those registers for the in-flight running sums
-  // and reads the operand from the K^T tile in LDS instead.
-  constexpr bool KD_REG = !XCD;
-  bf16x8 Kd[KD_REG ? NCOL : 1][KD_REG ? TC : 1];
+// ---- tile waves
+
+template <class G, bool CAUSAL, int MODE>
+struct TileRole {
+  static constexpr int KC = G::KC, ND = G::ND, MB = G::MB, NSUB = G::NSUB;
+  const MainParams& p;
+  Lds<G> L;
+  int tid, lane, a, l32, hh;
+  static constexpr bool VL = G::V_LDS;
+  bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
-  u32x4 stq[GPT][4], sto[GPT][4];  // staged next sub-tile
-  float stl = 0.0f, std_ = 0.0f;
+  f32x16 s, dp;  // first row block of the current sub-tile, carried over barrier X
 
-  auto col_of = [&](int kc) { return ND >= NW ? w * NCOL + kc : w % ND; };
-  auto row_of = [&](int kr) { return ND >= NW ? kr : w / ND + kr * (NW / ND); };
+  __device__ __forceinline__ TileRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    a = tid >> 6;
+    l32 = lane & 31;
+    hh = lane >> 5;
+  }
+
+  __device__ __forceinline__ void park(const Seg& sg, bool load) {
+    float* base = p.park + ((size_t)blockIdx.x * 2 + sg.slot) * (size_t)(2 * ND * 16 * G::NTA);
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float* x = base + (size_t)((n * 16 + i) * G::NTA + tid);
+        float* y = base + (size_t)(((ND + n) * 16 + i) * G::NTA + tid);
+        if (load) {
+          dKa[n][i] = *x;
+          dVa[n][i] = *y;
+        } else {
+          *x = dKa[n][i];
+          *y = dVa[n][i];
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void seg_begin(const Seg& sg) {
+    const int S = p.S;
+    const int key = min(sg.kv * G::T + 32 * a + l32, S - 1);  // keys past the end are masked
+    const bf16* kh = p.k + (size_t)sg.bh * S * G::D;
+    const bf16* vh = p.v + (size_t)sg.bh * S * G::D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const unsigned off = 2u * (unsigned)(key * G::D + 16 * c + 8 * hh);
+      Kr[c] = *at_bytes((const bf16x8*)kh, off);
+      const bf16x8 vv = *at_bytes((const bf16x8*)vh, off);
+      if constexpr (VL) *(bf16x8*)&L.v()[(32 * a + l32) * G::DP + 16 * c + 8 * hh] = vv;
+      else Vr[VL ? 0 : c] = vv;
+    }
+    // K^T for the dQ waves' operand
+    bf16* kt = L.kt();
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kt[(16 * c + 8 * hh + e) * G::TP + 32 * a + l32] = Kr[c][e];
+    }
+    if (sg.restore) {
+      park(sg, true);
+    } else {
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        dKa[n] = zero16();
+        dVa[n] = zero16();
+      }
+    }
+  }
+  __device__ __forceinline__ void seg_kd(const Seg&) {}
+  __device__ __forceinline__ void seg_stage(const Seg&) {}
+
+  // S and dP of row block m, turned into P and dS in place
+  __device__ __forceinline__ void sdp(int m, int buf, int q_base, int kv_base, bool need_mask) {
+    const bf16* Q = &L.q(buf)[(32 * m + l32) * G::DP + 8 * hh];
+    const bf16* O = &L.o(buf)[(32 * m + l32) * G::DP + 8 * hh];
+    const bf16* V = &L.v()[(32 * a + l32) * G::DP + 8 * hh];
+    s = zero16();
+    dp = zero16();
+    // operands one k-chunk ahead; the scheduling fences keep at most two
+    // chunks of operands live (the resident K/dK/dV leave little room)
+    bf16x8 qa[2], oa[2], vb[2];
+    qa[0] = *(const bf16x8*)&Q[0];
+    oa[0] = *(const bf16x8*)&O[0];
+    if constexpr (VL) vb[0] = *(const bf16x8*)&V[0];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (c + 1 < KC) {
+        qa[(c + 1) & 1] = *(const bf16x8*)&Q[16 * (c + 1)];
+        oa[(c + 1) & 1] = *(const bf16x8*)&O[16 * (c + 1)];
+        if constexpr (VL) vb[(c + 1) & 1] = *(const bf16x8*)&V[16 * (c + 1)];
+      }
+      s = mfma32(qa[c & 1], Kr[c], s);
+      dp = mfma32(oa[c & 1], VL ? vb[c & 1] : Vr[VL ? 0 : c], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float* Ls = L.lse(buf);
+    const float* Ds = L.dl(buf);
+    const int key_g = kv_base + 32 * a + l32;
+    if (need_mask) {  // diagonal tile of a causal mask, or the ragged last KV tile
+      const bool key_ok = key_g < p.S;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
+        const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * g + b;
+          const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
+          float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+          const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
+          pv = vis ? pv : 0.0f;
+          s[i] = pv;
+          dp[i] = pv * (dp[i] - D4[b]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
+        const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * g + b;
+          const float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+          s[i] = pv;
+          dp[i] = pv * (dp[i] - D4[b]);
+        }
+      }
+    }
+  }
+
+  // dS^T of row block m to LDS; dV += P^T dO and dK += dS^T Q
+  __device__ __forceinline__ void accumulate(int m) {
+    const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
+    const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
+    bf16* drow = &L.dst()[(32 * a + l32) * G::SP + 32 * m + 4 * hh];  // four consecutive queries per write
+    *(bf16x4*)(drow + 0) = __builtin_shufflevector(db0, db0, 0, 1, 2, 3);
+    *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
+    *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
+    *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
+    const bf16* QT = &L.qt()[l32 * G::BRP + 32 * m + 8 * hh];
+    const bf16* OT = &L.ot()[l32 * G::BRP + 32 * m + 8 * hh];
+    bf16x8 ov[2][2], qv[2][2];  // B operands one feature block ahead
+    ov[0][0] = *(const bf16x8*)&OT[0];
+    ov[0][1] = *(const bf16x8*)&OT[16];
+    qv[0][0] = *(const bf16x8*)&QT[0];
+    qv[0][1] = *(const bf16x8*)&QT[16];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+      if (n + 1 < ND) {
+        const int ro = 32 * (n + 1) * G::BRP;
+        ov[(n + 1) & 1][0] = *(const bf16x8*)&OT[ro];
+        ov[(n + 1) & 1][1] = *(const bf16x8*)&OT[ro + 16];
+        qv[(n + 1) & 1][0] = *(const bf16x8*)&QT[ro];
+        qv[(n + 1) & 1][1] = *(const bf16x8*)&QT[ro + 16];
+      }
+      dVa[n] = mfma32(pb0, ov[n & 1][0], dVa[n]);
+      dVa[n] = mfma32(pb1, ov[n & 1][1], dVa[n]);
+      dKa[n] = mfma32(db0, qv[n & 1][0], dKa[n]);
+      dKa[n] = mfma32(db1, qv[n & 1][1], dKa[n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  __device__ __forceinline__ void where(const Seg& sg, int i, int& q_base, int& kv_base, bool& need_mask) {
+    const Task task = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + i / NSUB);
+    q_base = task.q * G::T + (i % NSUB) * G::BR;
+    kv_base = sg.kv * G::T;
+    need_mask = (CAUSAL && task.q == sg.kv) || (kv_base + G::T > p.S);
+  }
+
+  __device__ __forceinline__ void part1(const Seg& sg, int i) {
+    int q_base, kv_base;
+    bool need_mask;
+    where(sg, i, q_base, kv_base, need_mask);
+    sdp(0, i & 1, q_base, kv_base, need_mask);
+  }
+
+  __device__ __forceinline__ void part2(const Seg& sg, int i) {
+    int q_base, kv_base;
+    bool need_mask;
+    where(sg, i, q_base, kv_base, need_mask);
+    accumulate(0);
+#pragma unroll
+    for (int m = 1; m < MB; ++m) {
+      sdp(m, i & 1, q_base, kv_base, need_mask);
+      accumulate(m);
+    }
+  }
+
+  __device__ __forceinline__ void seg_end(const Seg& sg) {
+    if (sg.keep) {
+      park(sg, false);
+      return;
+    }
+    const int S = p.S;
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = sg.kv * G::T + 32 * a + 8 * (i / 4) + 4 * hh + (i % 4);
+        if (key < S) {
+          const size_t off = ((size_t)sg.bh * S + key) * G::D + 32 * n + l32;
+          p.dk[off] = to_bf16(dKa[n][i] * p.scale);
+          p.dv[off] = to_bf16(dVa[n][i]);
+        }
+      }
+    }
+  }
+};
+
+// ---- dQ waves
+
+template <class G, bool CAUSAL, int MODE>
+struct DqRole {
+  static constexpr bool ATOMIC = MODE == MODE_ATOMIC;
+  static constexpr bool XCD = MODE == MODE_XCD;
+  static constexpr int QBW = G::QBW, TC = G::TC, GPT = G::GPT, NSUB = G::NSUB, BR = G::BR, D = G::D;
+  const MainParams& p;
+  Lds<G> L;
+  int tb, lane, b, l32, hh, mb, nb0;
+  bf16x8 Kd[QBW][TC];   // B operand of dQ: this wave's feature columns, all keys of the tile
+  bf16x8 dsA[TC];       // A operand of dQ: dS rows of this wave's row block
+  u32x4 stq[GPT][4], sto[GPT][4];  // staged query sub-tile
+  float stl = 0.0f, std_ = 0.0f;
+  int pend = -1;  // counter whose increment this wave still owes
+
+  __device__ __forceinline__ DqRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
+    tb = threadIdx.x - G::NTA;
+    lane = tb & 63;
+    b = tb >> 6;
+    l32 = lane & 31;
+    hh = lane >> 5;
+    constexpr int per_row = G::ND / QBW;
+    mb = b / per_row;
+    nb0 = QBW * (b % per_row);
+  }
+
+  __device__ __forceinline__ int sub_row0(const Seg& sg, int i) const {
+    const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + i / NSUB);
+    return t.q * G::T + (i % NSUB) * BR;
+  }
 
   // Rows past the end of the sequence are read as copies of the last row: the
   // masks give them P = 0 exactly, so a finite duplicate contributes nothing.
-  auto stage_load = [&](int bh, int qrow0) {
-    const bf16* qh = p.q + (size_t)bh * S * D;     // uniform head bases
+  __device__ __forceinline__ void stage_load(int bh, int qrow0) {
+    const int S = p.S;
+    const bf16* qh = p.q + (size_t)bh * S * D;  // uniform head bases
     const bf16* oh = p.dout + (size_t)bh * S * D;
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
-      const int gi = tid + g * NT;
+      const int gi = tb + g * G::NTB;
       const int qg = gi % (BR / 4), dg = gi / (BR / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -190,113 +457,223 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
         sto[g][rr] = *at_bytes((const u32x4*)oh, off);
       }
     }
-    if (tid < BR) {
-      const float* lh = p.lse2 + (size_t)bh * p.S_pad;
-      const float* dh = p.delta + (size_t)bh * p.S_pad;
-      stl = *at_bytes(lh, 4u * (unsigned)(qrow0 + tid));
-      std_ = *at_bytes(dh, 4u * (unsigned)(qrow0 + tid));
+    if (tb < BR) {
+      stl = *at_bytes(p.lse2 + (size_t)bh * p.S_pad, 4u * (unsigned)(qrow0 + tb));
+      std_ = *at_bytes(p.delta + (size_t)bh * p.S_pad, 4u * (unsigned)(qrow0 + tb));
     }
-  };
+  }
 
-  auto stage_store = [&]() {
+  __device__ __forceinline__ void write_rm(int buf) {
+    bf16* Q = L.q(buf);
+    bf16* O = L.o(buf);
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
-      const int gi = tid + g * NT;
+      const int gi = tb + g * G::NTB;
       const int qg = gi % (BR / 4), dg = gi / (BR / 4);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        *(u32x4*)&sQ[(qg * 4 + rr) * DP + dg * 8] = stq[g][rr];
-        *(u32x4*)&sO[(qg * 4 + rr) * DP + dg * 8] = sto[g][rr];
+        *(u32x4*)&Q[(qg * 4 + rr) * G::DP + dg * 8] = stq[g][rr];
+        *(u32x4*)&O[(qg * 4 + rr) * G::DP + dg * 8] = sto[g][rr];
       }
+    }
+    if (tb < BR) {
+      L.lse(buf)[tb] = stl;
+      L.dl(buf)[tb] = std_;
+    }
+  }
+
+  __device__ __forceinline__ void write_tr() {
+    bf16* QT = L.qt();
+    bf16* OT = L.ot();
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int gi = tb + g * G::NTB;
+      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
       const int pos = quad_pos(qg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bf16x4 tq, to;
+        // feature e of the four staged rows, as two packed pairs
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int wd = e >> 1;
+        u32x2 tq, to;
+        tq[0] = __builtin_amdgcn_perm(stq[g][1][wd], stq[g][0][wd], sel);
+        tq[1] = __builtin_amdgcn_perm(stq[g][3][wd], stq[g][2][wd], sel);
+        to[0] = __builtin_amdgcn_perm(sto[g][1][wd], sto[g][0][wd], sel);
+        to[1] = __builtin_amdgcn_perm(sto[g][3][wd], sto[g][2][wd], sel);
+        *(u32x2*)&QT[(dg * 8 + e) * G::BRP + pos] = tq;
+        *(u32x2*)&OT[(dg * 8 + e) * G::BRP + pos] = to;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void read_ds() {
+    const int grp = lane >> 4, gi = lane & 15;
+    const bf16* base =
+        &L.dst()[(8 * (grp >> 1) + (gi >> 2)) * G::SP + 32 * mb + 16 * (grp & 1) + 4 * (gi & 3)];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          tq[rr] = __builtin_bit_cast(bf16x8, stq[g][rr])[e];
-          to[rr] = __builtin_bit_cast(bf16x8, sto[g][rr])[e];
+    for (int c = 0; c < TC; ++c)
+      dsA[c] = cat44(lds_read_tr(base + 16 * c * G::SP), lds_read_tr(base + (16 * c + 4) * G::SP));
+  }
+
+  __device__ __forceinline__ void release() {
+    if (!ATOMIC && pend >= 0) {
+      wait_vmem();  // this wave's dQ updates have completed
+      if (lane == 0) __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pend = -1;
+    }
+  }
+
+  __device__ __forceinline__ void seg_begin(const Seg& sg) { stage_load(sg.bh, sub_row0(sg, 0)); }
+
+  __device__ __forceinline__ void seg_kd(const Seg&) {
+    const bf16* kt = L.kt();
+#pragma unroll
+    for (int j = 0; j < QBW; ++j) {
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+        Kd[j][c] = *(const bf16x8*)&kt[(32 * (nb0 + j) + l32) * G::TP + 16 * c + 8 * hh];
+    }
+  }
+
+  __device__ __forceinline__ void seg_stage(const Seg& sg) {
+    write_rm(0);
+    write_tr();
+    if (sg.n > 1) stage_load(sg.bh, sub_row0(sg, 1));
+  }
+
+  // The hand-off of sub-tile j runs in three steps spread over the next
+  // interval so that its memory latencies overlap other work:
+  //   acquire (before barrier X): dQ = dS K into registers; wait for the turn;
+  //            start the loads of the running sum;
+  //   commit  (after barrier X):  add and store (or the atomic RMWs);
+  //   release (next interval):    once the stores have completed, count this
+  //            wave's contribution on the sub-tile's counter.
+  f32x16 acc[QBW], prev[QBW];
+  int h_cidx = 0, h_r = 0;
+  bool h_last = true;
+  float* h_row = nullptr;
+
+  __device__ __forceinline__ unsigned elem_off(int j, int e) const {
+    return 4u * (unsigned)((32 * mb + 4 * hh + 8 * (e / 4) + (e % 4)) * D + 32 * (nb0 + j) + l32);
+  }
+
+  __device__ __forceinline__ void acquire(const Seg& sg, int j) {
+#pragma unroll
+    for (int x = 0; x < QBW; ++x) {
+      acc[x] = zero16();
+#pragma unroll
+      for (int c = 0; c < TC; ++c) acc[x] = mfma32(dsA[c], Kd[x][c], acc[x]);
+    }
+    const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + j / NSUB);
+    h_cidx = sg.bh * p.n_qsub + t.q * NSUB + j % NSUB;
+    h_r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, t.q, sg.kv);
+    h_last = ATOMIC ? true : (h_r == sched_contributors(p.N, CAUSAL, t.q) - 1);
+    h_row = p.dq_ws + ((size_t)sg.bh * p.S_pad + t.q * G::T + (j % NSUB) * BR) * D;  // uniform
+    if (ATOMIC || h_r == 0) return;
+    // wait until every wave of the previous contributor has released
+    const int target = G::NB * h_r;
+    int seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t it = 0;
+    while (__builtin_amdgcn_readfirstlane(seen) != target) {
+      if (++it >= p.wait_limit) {
+        __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (XCD) {
+      // Every contributor of this tile runs on this XCD, so its L2 holds the
+      // accumulator coherently for all of them: drop this CU's write-through
+      // L1 copies, then read the running sum.
+      asm volatile("buffer_inv sc0" ::: "memory");
+#pragma unroll
+      for (int x = 0; x < QBW; ++x) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) prev[x][e] = *at_bytes(h_row, elem_off(x, e));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void commit() {
+    if (ATOMIC) {
+#pragma unroll
+      for (int x = 0; x < QBW; ++x) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) atomicAdd(at_bytes(h_row, elem_off(x, e)), acc[x][e]);
+      }
+      return;
+    }
+    if (XCD) {
+      // (the first contributor stores its partial as it is)
+#pragma unroll
+      for (int x = 0; x < QBW; ++x) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          *at_bytes(h_row, elem_off(x, e)) = h_r > 0 ? prev[x][e] + acc[x][e] : acc[x][e];
+      }
+    } else {
+      // Device-scope atomic RMWs, serialised by the counters: each element
+      // receives the same fp32 additions in the same order on every run; the
+      // first contributor swaps its value in.
+#pragma unroll
+      for (int x = 0; x < QBW; ++x) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (h_r == 0)
+            __hip_atomic_exchange(at_bytes(h_row, elem_off(x, e)), acc[x][e], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+          else
+            __hip_atomic_fetch_add(at_bytes(h_row, elem_off(x, e)), acc[x][e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        *(bf16x4*)&sQT[(dg * 8 + e) * BRP + pos] = tq;
-        *(bf16x4*)&sOT[(dg * 8 + e) * BRP + pos] = to;
       }
     }
-    if (tid < BR) {
-      sL[tid] = stl;
-      sDl[tid] = std_;
-    }
-  };
+    if (!h_last) pend = h_cidx;
+  }
 
-  // K/V of KV tile kv into registers (and K^T through LDS for the dQ operand)
-  auto load_kv = [&](int bh, int kv) {
-    const int key = min(kv * T + 32 * w + l32, S - 1);  // keys past the end are masked
-    const bf16* kh = p.k + (size_t)bh * S * D;
-    const bf16* vh = p.v + (size_t)bh * S * D;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const unsigned off = 2u * (unsigned)(key * D + 16 * c + 8 * hh);
-      Kr[c] = *at_bytes((const bf16x8*)kh, off);
-      Vr[c] = *at_bytes((const bf16x8*)vh, off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sKT[(16 * c + 8 * hh + e) * TP + 32 * w + l32] = Kr[c][e];
+  __device__ __forceinline__ void part1(const Seg& sg, int i) {
+    if (i > 0) {
+      // (order matters for the memory counters: the staged registers are
+      // consumed before the running-sum loads are issued, and those before the
+      // next staging loads, so no step waits for a younger load)
+      read_ds();
+      release();  // wait for the previous sub-tile's stores, before any new load is issued
+      write_tr();
+      acquire(sg, i - 1);
+      if (i + 1 < sg.n) stage_load(sg.bh, sub_row0(sg, i + 1));
     }
-    __syncthreads();
-    if (KD_REG) {
-#pragma unroll
-      for (int kc = 0; kc < NCOL; ++kc) {
-#pragma unroll
-        for (int c = 0; c < TC; ++c)
-          Kd[KD_REG ? kc : 0][KD_REG ? c : 0] = *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
-      }
-    }
-  };
+  }
 
-  auto finalize_kv = [&](int bh, int kv) {
-#pragma unroll
-    for (int n = 0; n < ND; ++n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kv * T + 32 * w + 8 * (i / 4) + 4 * hh + (i % 4);
-        if (key < S) {
-          const size_t off = ((size_t)bh * S + key) * D + 32 * n + l32;
-          p.dk[off] = to_bf16(dKa[n][i] * p.scale);
-          p.dv[off] = to_bf16(dVa[n][i]);
-        }
-      }
-    }
-  };
+  __device__ __forceinline__ void part2(const Seg& sg, int i) {
+    if (i > 0) commit();
+    if (i + 1 < sg.n) write_rm((i + 1) & 1);
+  }
 
-  // Symmetric Shift parking: one slot per (workgroup, tile of the pair)
-  auto park_acc = [&](int slot, bool load) {
-    float* base = p.park + ((size_t)blockIdx.x * 2 + slot) * (size_t)(2 * ND * 16 * NT);
-#pragma unroll
-    for (int n = 0; n < ND; ++n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float* a = base + (size_t)((n * 16 + i) * NT + tid);
-        float* b = base + (size_t)(((ND + n) * 16 + i) * NT + tid);
-        if (load) {
-          dKa[n][i] = *a;
-          dVa[n][i] = *b;
-        } else {
-          *a = dKa[n][i];
-          *b = dVa[n][i];
-        }
-      }
-    }
-    wait_vmem();
-  };
+  __device__ __forceinline__ void seg_end(const Seg& sg) {
+    read_ds();
+    release();
+    acquire(sg, sg.n - 1);
+    commit();
+    release();
+  }
+};
 
+// ---- the shared unit / segment / sub-tile skeleton (identical barrier sequence for both roles)
+
+template <class G, bool CAUSAL, int MODE, class Role>
+__device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, Role& role) {
+  constexpr bool XCD = MODE == MODE_XCD;
   int xq = 0;  // this workgroup's XCD, the queue it takes units from
   if (XCD) {
     unsigned x;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
     xq = (int)(x & (kMaxQueues - 1));
   }
-
+  int* sUnit = L.unit();
   for (;;) {
-    __syncthreads();
-    if (tid == 0) {
+    lds_barrier();
+    if (threadIdx.x == 0) {
       if (!XCD) {
         const int u = atomicAdd(&p.header[0], 1);
         sUnit[0] = u < p.n_units ? u / p.n_workers : p.BH;
@@ -330,257 +707,70 @@ __global__ void __launch_bounds__(T / 32 * 64, 1) bwd_main_kernel(MainParams p) 
         sUnit[1] = wk;
       }
     }
-    __syncthreads();
-    const int bh = sUnit[0];
-    const int wk = sUnit[1];
+    lds_barrier();
+    const int bh = __builtin_amdgcn_readfirstlane(sUnit[0]);
+    const int wk = __builtin_amdgcn_readfirstlane(sUnit[1]);
     if (bh >= p.BH) break;
     const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
-    const int total = ntasks * NSUB;
 
-    // the (at most two) KV tiles of this unit and the last task of each
-    int tileA = -1, tileB = -1, lastA = -1, lastB = -1;
+    // the (at most two) KV tiles of this unit and the last task on each
+    int tileA = -1, lastA = -1, lastB = -1;
     for (int t = 0; t < ntasks; ++t) {
       const int kv = sched_task(p.N, CAUSAL, p.sched, wk, t).kv;
       if (tileA < 0 || kv == tileA) {
         tileA = kv;
         lastA = t;
       } else {
-        tileB = kv;
         lastB = t;
       }
     }
-    int cur_kv = -1;
     bool parkedA = false, parkedB = false;
-    int pend = -1;  // counter whose increment is still owed (its RMWs are in flight)
+    for (int t0 = 0; t0 < ntasks;) {
+      const int kv = sched_task(p.N, CAUSAL, p.sched, wk, t0).kv;
+      int t1 = t0 + 1;
+      while (t1 < ntasks && sched_task(p.N, CAUSAL, p.sched, wk, t1).kv == kv) ++t1;
+      Seg sg;
+      sg.bh = bh;
+      sg.wk = wk;
+      sg.t0 = t0;
+      sg.n = (t1 - t0) * G::NSUB;
+      sg.kv = kv;
+      const bool isA = kv == tileA;
+      sg.slot = isA ? 0 : 1;
+      sg.restore = isA ? parkedA : parkedB;
+      sg.keep = (isA ? lastA : lastB) >= t1;
+      if (isA) parkedA = sg.keep;
+      else parkedB = sg.keep;
 
-    {
-      const Task t0 = sched_task(p.N, CAUSAL, p.sched, wk, 0);
-      stage_load(bh, t0.q * T);
-      stage_store();
-      if (total > 1) {
-        const Task t1 = sched_task(p.N, CAUSAL, p.sched, wk, 1 / NSUB);
-        stage_load(bh, t1.q * T + (1 % NSUB) * BR);
+      role.seg_begin(sg);  // tile waves: K/V, K^T to LDS, accumulators; dQ waves: load sub-tile 0
+      lds_barrier();
+      role.seg_kd(sg);     // dQ waves: K columns from LDS
+      lds_barrier();
+      role.seg_stage(sg);  // dQ waves: sub-tile 0 into LDS, load sub-tile 1
+      lds_barrier();
+      for (int i = 0; i < sg.n; ++i) {
+        role.part1(sg, i);
+        lds_barrier();  // X
+        role.part2(sg, i);
+        lds_barrier();  // Y
       }
+      role.seg_end(sg);    // tile waves: park or write dK/dV; dQ waves: last sub-tile's dQ
+      t0 = t1;
     }
+  }
+}
 
-    for (int idx = 0; idx < total; ++idx) {
-      const int t = idx / NSUB;
-      const int sidx = idx % NSUB;
-      const Task task = sched_task(p.N, CAUSAL, p.sched, wk, t);
-      const int qi = task.q, kj = task.kv;
-
-      if (kj != cur_kv) {
-        if (cur_kv >= 0) {
-          const bool isA = (cur_kv == tileA);
-          if (t <= (isA ? lastA : lastB)) {
-            park_acc(isA ? 0 : 1, false);
-            if (isA) parkedA = true; else parkedB = true;
-          } else {
-            finalize_kv(bh, cur_kv);
-          }
-        }
-        __syncthreads();
-        load_kv(bh, kj);
-        const bool isA = (kj == tileA);
-        if (isA ? parkedA : parkedB) {
-          park_acc(isA ? 0 : 1, true);
-          if (isA) parkedA = false; else parkedB = false;
-        } else {
-#pragma unroll
-          for (int n = 0; n < ND; ++n) {
-            dKa[n] = zero16();
-            dVa[n] = zero16();
-          }
-        }
-        cur_kv = kj;
-      }
-
-      const int q_base = qi * T + sidx * BR;
-      const int kv_base = kj * T;
-      __syncthreads();  // staged sub-tile visible
-
-      // ---- S = Q K^T, dP = dO V^T, P, dS; dV += P^T dO, dK += dS^T Q
-      const int key_g = kv_base + 32 * w + l32;
-      const bool key_ok = key_g < S;
-      const bool need_mask = (CAUSAL && qi == kj) || (kv_base + T > S);
-#pragma unroll 1
-      for (int m = 0; m < MB; ++m) {
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const bf16x8 qa = *(const bf16x8*)&sQ[(32 * m + l32) * DP + 16 * c + 8 * hh];
-          const bf16x8 oa = *(const bf16x8*)&sO[(32 * m + l32) * DP + 16 * c + 8 * hh];
-          s = mfma32(qa, Kr[c], s);
-          dp = mfma32(oa, Vr[c], dp);
-        }
-        if (need_mask) {  // diagonal tile of a causal mask, or the ragged last KV tile
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
-            const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int i = 4 * a + b;
-              const int q_g = q_base + 32 * m + 8 * a + 4 * hh + b;
-              float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
-              const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
-              pv = vis ? pv : 0.0f;
-              s[i] = pv;
-              dp[i] = pv * (dp[i] - D4[b]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const f32x4 L4 = *(const f32x4*)&sL[32 * m + 8 * a + 4 * hh];
-            const f32x4 D4 = *(const f32x4*)&sDl[32 * m + 8 * a + 4 * hh];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int i = 4 * a + b;
-              const float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
-              s[i] = pv;
-              dp[i] = pv * (dp[i] - D4[b]);
-            }
-          }
-        }
-        const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
-        const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
-        // dS^T: four consecutive queries per 8-byte write
-        bf16* drow = &sdST[(32 * w + l32) * SP + 32 * m + 4 * hh];
-        *(bf16x4*)(drow + 0) = __builtin_shufflevector(db0, db0, 0, 1, 2, 3);
-        *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
-        *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
-        *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          const int ro = (32 * n + l32) * BRP + 32 * m + 8 * hh;
-          dVa[n] = mfma32(pb0, *(const bf16x8*)&sOT[ro], dVa[n]);
-          dVa[n] = mfma32(pb1, *(const bf16x8*)&sOT[ro + 16], dVa[n]);
-          dKa[n] = mfma32(db0, *(const bf16x8*)&sQT[ro], dKa[n]);
-          dKa[n] = mfma32(db1, *(const bf16x8*)&sQT[ro + 16], dKa[n]);
-        }
-      }
-      wait_vmem();      // this wave's earlier dQ RMWs and staging loads have completed
-      __syncthreads();  // dS^T complete; staged Q/dO no longer read; all earlier RMWs done
-
-      if (!ATOMIC && pend >= 0 && tid == 0)
-        __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      pend = -1;
-      if (idx + 1 < total) {
-        stage_store();
-        if (!XCD && idx + 2 < total) {  // prefetch now: it lands during the dQ phase and the next S/dP
-          const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, (idx + 2) / NSUB);
-          stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
-        }
-      }
-
-      // ---- dQ partial of this sub-tile and its ordered hand-off
-      const int cidx = bh * p.n_qsub + qi * NSUB + sidx;
-      const int r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, qi, kj);
-      const bool last = ATOMIC ? true : (r == sched_contributors(p.N, CAUSAL, qi) - 1);
-      int seen = r;
-      if (!ATOMIC && r > 0 && tid == 0)  // poll early
-        seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      float* wsrow = p.dq_ws + ((size_t)bh * p.S_pad + q_base) * D;  // uniform
-
-      // Turn-taking: wait until the previous contributor's update is complete.
-      auto wait_turn = [&]() {
-        if (tid == 0) {
-          uint32_t it = 0;
-          while (seen != r) {
-            if (++it >= p.wait_limit) {
-              __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            seen = __hip_atomic_load(&p.counters[cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        __syncthreads();
-      };
-      auto dq_block = [&](int kc, int mb) {
-        f32x16 acc = zero16();
-        const int grp = lane >> 4, gi = lane & 15;
-        const bf16* base = &sdST[(8 * (grp >> 1) + (gi >> 2)) * SP + 32 * mb + 16 * (grp & 1) + 4 * (gi & 3)];
-#pragma unroll
-        for (int c = 0; c < TC; ++c) {
-          const bf16x8 a = cat44(lds_read_tr(base + 16 * c * SP), lds_read_tr(base + (16 * c + 4) * SP));
-          const bf16x8 kb = KD_REG ? Kd[KD_REG ? kc : 0][KD_REG ? c : 0]
-                                   : *(const bf16x8*)&sKT[(32 * col_of(kc) + l32) * TP + 16 * c + 8 * hh];
-          acc = mfma32(a, kb, acc);
-        }
-        return acc;
-      };
-      auto elem_off = [&](int nb, int mb, int i) {
-        return 4u * (unsigned)((32 * mb + 4 * hh + 8 * (i / 4) + (i % 4)) * D + 32 * nb + l32);
-      };
-
-      if (XCD) {
-        // Every contributor of this tile runs on this XCD, so its L2 holds the
-        // accumulator coherently for all of them. After our turn, drop this
-        // CU's write-through L1 copies, start the loads of the running sum,
-        // compute the partial while they are in flight, then add and store.
-        // (The first contributor adds to 0, which only turns -0 into +0.)
-        static_assert(!XCD || NCOL * NROW == 2, "XCD-local hand-off is written for two dQ blocks per wave");
-        const int nb0 = col_of(0), mb0 = row_of(0);
-        const int nb1 = col_of(NCOL > 1 ? 1 : 0), mb1 = row_of(NCOL > 1 ? 0 : 1);
-        const f32x16 acc0 = dq_block(0, mb0);  // overlaps the early poll
-        float prev0[16], prev1[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) prev0[i] = prev1[i] = 0.0f;
-        if (r > 0) {
-          wait_turn();
-          asm volatile("buffer_inv sc0" ::: "memory");
-#pragma unroll
-          for (int i = 0; i < 16; ++i) prev0[i] = *at_bytes(wsrow, elem_off(nb0, mb0, i));
-#pragma unroll
-          for (int i = 0; i < 16; ++i) prev1[i] = *at_bytes(wsrow, elem_off(nb1, mb1, i));
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the second block's MFMAs
-        const f32x16 acc1 = dq_block(NCOL > 1 ? 1 : 0, mb1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) *at_bytes(wsrow, elem_off(nb0, mb0, i)) = prev0[i] + acc0[i];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) *at_bytes(wsrow, elem_off(nb1, mb1, i)) = prev1[i] + acc1[i];
-      } else {
-        // Device-scope atomic RMWs (the deterministic mode serialises them with
-        // the counters, so each element receives the same fp32 additions in
-        // the same order on every run; the first contributor swaps its value in).
-#pragma unroll
-        for (int kc = 0; kc < NCOL; ++kc) {
-#pragma unroll 1
-          for (int kr = 0; kr < NROW; ++kr) {
-            const int nb = col_of(kc), mb = row_of(kr);
-            const f32x16 acc = dq_block(kc, mb);
-            if (!ATOMIC && r > 0 && kc == 0 && kr == 0) wait_turn();
-            if (!ATOMIC && r == 0) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                __hip_atomic_exchange(at_bytes(wsrow, elem_off(nb, mb, i)), acc[i], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i)
-                __hip_atomic_fetch_add(at_bytes(wsrow, elem_off(nb, mb, i)), acc[i], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
-      }
-      if (!ATOMIC && !last) pend = cidx;
-      // XCD-local mode prefetches here, keeping the dQ phase free of staging
-      // registers; the loads still have the whole next S/dP phase to land
-      if (XCD && idx + 2 < total) {
-        const Task n2 = sched_task(p.N, CAUSAL, p.sched, wk, (idx + 2) / NSUB);
-        stage_load(bh, n2.q * T + ((idx + 2) % NSUB) * BR);
-      }
-    }
-    if (pend >= 0) {  // the unit's last hand-off
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (cur_kv >= 0) finalize_kv(bh, cur_kv);
+template <int D, int T, int BR, bool CAUSAL, int MODE>
+__global__ void __launch_bounds__(T / 16 * 64) bwd_main_kernel(MainParams p) {
+  using G = Geo<D, T, BR>;
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  const Lds<G> L{smem};
+  if ((int)(threadIdx.x >> 6) < G::NA) {
+    TileRole<G, CAUSAL, MODE> role(p, L);
+    run_units<G, CAUSAL, MODE>(p, L, role);
+  } else {
+    DqRole<G, CAUSAL, MODE> role(p, L);
+    run_units<G, CAUSAL, MODE>(p, L, role);
   }
 }
 
@@ -611,7 +801,7 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
 
 template <int D, int T, int BR, bool CAUSAL, int MODE>
 static hipError_t launch_main(const MainParams& mp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_main_kernel<D, T, BR, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T / 32 * 64), 0, stream,
+  hipLaunchKernelGGL((bwd_main_kernel<D, T, BR, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T / 16 * 64), 0, stream,
                      mp);
   return hipGetLastError();
 }
@@ -621,7 +811,7 @@ static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int
                               int* xcd_out) {
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, bwd_main_kernel<D, T, BR, CAUSAL, MODE_DEVICE>, T / 32 * 64, 0);
+      &per_cu, bwd_main_kernel<D, T, BR, CAUSAL, MODE_DEVICE>, T / 16 * 64, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   long long grid = (long long)num_cu * per_cu;
@@ -636,14 +826,10 @@ static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int
   // workgroups. Cyclic schedules need all workers of a head resident there.
   const int n_xcd = (num_cu >= 64 && num_cu % 8 == 0) ? 8 : 1;
   const long long per_xcd = grid / n_xcd;
-  // (the XCD-local hand-off is written for two dQ blocks per wave)
-  constexpr bool kXcdShape = (BR / 32) * (D / 32) == 2 * (T / 32);
-  const bool xcd = kXcdShape && !atomic && protocol != DQ_DEVICE_ATOMIC && (!cyclic || mp.n_workers <= per_xcd);
+  const bool xcd = !atomic && protocol != DQ_DEVICE_ATOMIC && (!cyclic || mp.n_workers <= per_xcd);
   *xcd_out = xcd ? 1 : 0;
   if (atomic) return launch_main<D, T, BR, CAUSAL, MODE_ATOMIC>(mp, (int)grid, stream);
-  if constexpr (kXcdShape) {
-    if (xcd) return launch_main<D, T, BR, CAUSAL, MODE_XCD>(mp, (int)grid, stream);
-  }
+  if (xcd) return launch_main<D, T, BR, CAUSAL, MODE_XCD>(mp, (int)grid, stream);
   return launch_main<D, T, BR, CAUSAL, MODE_DEVICE>(mp, (int)grid, stream);
 }
 
