@@ -553,9 +553,16 @@ struct DqRole {
   bool h_last = true;
   float* h_row = nullptr;
 
-  __device__ __forceinline__ unsigned elem_off(int j, int e) const {
-    return 4u * (unsigned)((32 * mb + 4 * hh + 8 * (e / 4) + (e % 4)) * D + 32 * (nb0 + j) + l32);
-  }
+  // The dQ accumulator is stored in the MFMA's own register order: per query
+  // sub-tile, 32 x 32 blocks (row block mb, feature block nb) of 1024 floats.
+  // Every contributor of a block holds it in the same lanes, so
+  //  - XCD-local mode, "quad-major": accumulators 4g..4g+3 of lane l at
+  //    (g * 64 + l) * 4: each 16-byte access of a wave covers 1 KB;
+  //  - atomic modes, "element-major": accumulator e of lane l at e * 64 + l:
+  //    each atomic instruction covers 256 contiguous bytes.
+  __device__ __forceinline__ unsigned blk_base(int j) const { return 4096u * (unsigned)(mb * G::ND + nb0 + j); }
+  __device__ __forceinline__ unsigned elem_off(int j, int e) const { return blk_base(j) + 4u * (64 * e + lane); }
+  __device__ __forceinline__ unsigned quad_off(int j, int g) const { return blk_base(j) + 16u * (64 * g + lane); }
 
   __device__ __forceinline__ void acquire(const Seg& sg, int j) {
 #pragma unroll
@@ -590,7 +597,11 @@ struct DqRole {
 #pragma unroll
       for (int x = 0; x < QBW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) prev[x][e] = *at_bytes(h_row, elem_off(x, e));
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = *at_bytes((const f32x4*)h_row, quad_off(x, g));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) prev[x][4 * g + k] = v[k];
+        }
       }
     }
   }
@@ -609,8 +620,12 @@ struct DqRole {
 #pragma unroll
       for (int x = 0; x < QBW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          *at_bytes(h_row, elem_off(x, e)) = h_r > 0 ? prev[x][e] + acc[x][e] : acc[x][e];
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = h_r > 0 ? prev[x][4 * g + k] + acc[x][4 * g + k] : acc[x][4 * g + k];
+          *at_bytes((f32x4*)h_row, quad_off(x, g)) = v;
+        }
       }
     } else {
       // Device-scope atomic RMWs, serialised by the counters: each element
@@ -779,20 +794,33 @@ __global__ void __launch_bounds__(T / 16 * 64) bwd_main_kernel(MainParams p) {
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, long long BH, int S,
-                                                       int S_pad, float scale) {
-  const long long n4 = BH * S * (D / 4);
+                                                       int S_pad, int BR, int quad_major, float scale) {
+  // dq_ws holds, per query sub-tile of BR rows, 32 x 32 blocks in MFMA register
+  // order (see the dQ waves: quad-major or element-major within a block); one
+  // thread converts accumulators 4g..4g+3 of one lane: four consecutive rows
+  // of one feature column.
+  constexpr int ND = D / 32;
+  const long long n4 = BH * S_pad * (D / 4);
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (long long)gridDim.x * blockDim.x) {
-    const long long e = i * 4;
-    const long long row = e / D;  // bh * S + s
-    const int col = (int)(e % D);
-    const long long bh = row / S;
-    const int s = (int)(row % S);
-    const f32x4 v = *(const f32x4*)(dq_ws + ((bh * S_pad + s) * D + col));
-    bf16x4 o;
+    const long long sub = i / (BR * D / 4);  // bh * (S_pad / BR) + sub-tile
+    const int r = (int)(i % (BR * D / 4));
+    const int blk = r >> 8, g = (r >> 6) & 3, lane = r & 63;
+    const int col = 32 * (blk % ND) + (lane & 31);
+    const int row0 = 32 * (blk / ND) + 8 * g + 4 * (lane >> 5);
+    const long long bh = sub / (S_pad / BR);
+    const int s0 = (int)(sub % (S_pad / BR)) * BR + row0;
+    f32x4 v;
+    if (quad_major) {
+      v = *(const f32x4*)(dq_ws + i * 4);
+    } else {
+      const float* b = dq_ws + (i - r) * 4 + blk * 1024 + 256 * g + lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = to_bf16(v[j] * scale);
-    *(bf16x4*)(dq + e) = o;
+      for (int k = 0; k < 4; ++k) v[k] = b[64 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (s0 + k < S) dq[(bh * S + s0 + k) * D + col] = to_bf16(v[k] * scale);
   }
 }
 
@@ -921,14 +949,14 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   }
 
   {
-    const long long want = (BH * a.S * (a.D / 4) + 255) / 256;
+    const long long want = (BH * a.S_pad * (a.D / 4) + 255) / 256;
     const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
     if (a.D == 64)
       hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.scale);
+                         a.S_pad, a.BR, xcd_local, a.scale);
     else
       hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.scale);
+                         a.S_pad, a.BR, xcd_local, a.scale);
     e = hipGetLastError();
   }
   return e;

@@ -35,6 +35,10 @@
 // the device and by attn_schedule_plan() on the host; no table is stored.
 #pragma once
 
+// (Every index below stays within [0, 2m) of the modulus m it is reduced by,
+// so a conditional subtraction replaces the remainder: no integer division in
+// the per-sub-tile scalar code.)
+
 #ifdef __HIPCC__
 #define ATTN_HD __host__ __device__ __forceinline__
 #else
@@ -42,6 +46,9 @@
 #endif
 
 namespace attn {
+
+// x mod m for x in [-m, 2m)
+ATTN_HD int wrap(int x, int m) { return x >= m ? x - m : (x < 0 ? x + m : x); }
 
 enum { SCHED_NAIVE = 0, SCHED_DESCENDING = 1, SCHED_SHIFT = 2, SCHED_SYMMETRIC_SHIFT = 3 };
 
@@ -77,12 +84,12 @@ ATTN_HD Task sched_task(int N, bool causal, int sched, int w, int t) {
       break;
     case SCHED_SHIFT:
       k.kv = w;
-      k.q = (w + t) % N;
+      k.q = wrap(w + t, N);
       break;
     default: {
       const int h = N / 2;
       if (t < h) {                 // phase 1: dense rectangle
-        k.q = h + (w + t) % h;
+        k.q = h + wrap(w + t, h);
         k.kv = w;
       } else if (t == h) {         // folded square, diagonal, upper-left task
         k.q = w;
@@ -91,7 +98,7 @@ ATTN_HD Task sched_task(int N, bool causal, int sched, int w, int t) {
         k.q = N - 1 - w;
         k.kv = N - 1 - w;
       } else {                     // folded square, off-diagonal
-        const int rho = (w + (t - h - 1)) % h;
+        const int rho = wrap(w + (t - h - 1), h);
         if (rho > w) {
           k.q = rho;
           k.kv = w;
@@ -113,11 +120,11 @@ ATTN_HD int sched_rank(int N, bool causal, int sched, int i, int j) {
   switch (sched) {
     case SCHED_NAIVE:
     case SCHED_DESCENDING: return j;
-    case SCHED_SHIFT: return ((i - j) % N + N) % N;
+    case SCHED_SHIFT: return wrap(i - j, N);
     default: {
       const int h = N / 2;
       if (i < h) return i - j;
-      if (j < h) return (((i - h - j) % h) + h) % h;
+      if (j < h) return wrap(i - h - j, h);
       if (j == i) return h;
       return j + 1;
     }
