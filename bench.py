@@ -185,8 +185,7 @@ def main():
     if args.schedules:
         scheds = args.schedules.split(",")
     else:
-        scheds = ["naive", "descending"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else []) + \
-                 ([] if w.causal else ["shift"])
+        scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else [])
     out = tuple(torch.empty_like(q) for _ in range(3))
     results = {}
     for s in scheds:

@@ -52,7 +52,6 @@ int check_shape(int B, int H, int S, int D, int mask, int schedule, int tile_req
   // index arithmetic on the device uses 32-bit unit and counter indices
   if (BH * N * (T / BR) >= (1ll << 31) || BH * N * T * D >= (1ll << 40)) return ATTN_ERR_UNSUPPORTED;
   if (deterministic) {
-    if (schedule == ATTN_SCHED_SHIFT && mask != ATTN_MASK_FULL) return ATTN_ERR_UNSUPPORTED;
     if (schedule == ATTN_SCHED_SYMMETRIC_SHIFT && (mask != ATTN_MASK_CAUSAL || (N % 2) != 0))
       return ATTN_ERR_UNSUPPORTED;
   }
@@ -206,7 +205,6 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
   if (mask != ATTN_MASK_FULL && mask != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_SYMMETRIC_SHIFT) return ATTN_ERR_INVALID_ARG;
   const bool causal = mask == ATTN_MASK_CAUSAL;
-  if (schedule == ATTN_SCHED_SHIFT && causal) return ATTN_ERR_UNSUPPORTED;
   if (schedule == ATTN_SCHED_SYMMETRIC_SHIFT && (!causal || n_tiles % 2)) return ATTN_ERR_UNSUPPORTED;
   const int nw = sched_workers(n_tiles, schedule);
   size_t n_tasks = 0;

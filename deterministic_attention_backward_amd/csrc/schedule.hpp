@@ -15,7 +15,11 @@
 //   SHIFT           §2.2 B, full mask: worker j starts at query tile j and
 //                   continues cyclically, so at every step each worker is on a
 //                   different dQ tile; dQ order = the order of those steps,
-//                   r(i, j) = (i - j) mod N.
+//                   r(i, j) = (i - j) mod N. Causal mask (the DASH abstract
+//                   credits Shift Scheduling for both masks): the same cyclic
+//                   walk with the fully masked query tiles 0..j-1 left out, so
+//                   worker j walks j, j+1, ..., N-1 and dQ tile i receives
+//                   KV tiles i, i-1, ..., 0 in that order: r(i, j) = i - j.
 //   SYMMETRIC_SHIFT §2.2 B, causal mask: worker p owns KV tiles p and N-1-p
 //                   (N even). Steps 0..N/2-1 cover the dense lower-left
 //                   rectangle (query tiles N/2..N-1 x KV tile p) with a cyclic
@@ -64,8 +68,8 @@ ATTN_HD int sched_workers(int N, int sched) { return sched == SCHED_SYMMETRIC_SH
 ATTN_HD int sched_num_tasks(int N, bool causal, int sched, int w) {
   switch (sched) {
     case SCHED_NAIVE:
-    case SCHED_DESCENDING: return causal ? N - w : N;
-    case SCHED_SHIFT: return N;
+    case SCHED_DESCENDING:
+    case SCHED_SHIFT: return causal ? N - w : N;
     default: return N + 1;
   }
 }
@@ -84,7 +88,7 @@ ATTN_HD Task sched_task(int N, bool causal, int sched, int w, int t) {
       break;
     case SCHED_SHIFT:
       k.kv = w;
-      k.q = wrap(w + t, N);
+      k.q = causal ? w + t : wrap(w + t, N);
       break;
     default: {
       const int h = N / 2;
@@ -120,7 +124,7 @@ ATTN_HD int sched_rank(int N, bool causal, int sched, int i, int j) {
   switch (sched) {
     case SCHED_NAIVE:
     case SCHED_DESCENDING: return j;
-    case SCHED_SHIFT: return wrap(i - j, N);
+    case SCHED_SHIFT: return causal ? i - j : wrap(i - j, N);
     default: {
       const int h = N / 2;
       if (i < h) return i - j;

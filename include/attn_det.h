@@ -59,7 +59,7 @@ typedef enum { ATTN_MASK_FULL = 0, ATTN_MASK_CAUSAL = 1 } attn_mask_t;
 typedef enum {
   ATTN_SCHED_NAIVE = 0,          /* ascending query tiles; dQ in KV-ascending order       */
   ATTN_SCHED_DESCENDING = 1,     /* Descending Q-Tile Iteration (DASH §2.2 A)             */
-  ATTN_SCHED_SHIFT = 2,          /* Shift Scheduling, full mask (DASH §2.2 B)             */
+  ATTN_SCHED_SHIFT = 2,          /* Shift Scheduling (DASH §2.2 B; abstract: both masks)  */
   ATTN_SCHED_SYMMETRIC_SHIFT = 3 /* Symmetric Shift, causal mask, even tile count (§2.2 B)*/
 } attn_schedule_t;
 
@@ -100,9 +100,10 @@ size_t attn_bwd_workspace_size(int B, int H, int S, int D, int mask, int schedul
  *   dK/dV in registers; dQ tile i is accumulated in fp32 in the order the
  *   schedule fixes, each contributor waiting for its turn on a per-tile
  *   counter. The dQ accumulation uses no floating-point atomics.
- *   schedule: attn_schedule_t. SHIFT needs ATTN_MASK_FULL; SYMMETRIC_SHIFT
- *   needs ATTN_MASK_CAUSAL and an even tile count; other combinations return
- *   ATTN_ERR_UNSUPPORTED.
+ *   schedule: attn_schedule_t. NAIVE, DESCENDING and SHIFT take either
+ *   mask (SHIFT on a causal mask: worker j walks query tiles j..N-1, dQ tile i
+ *   accumulates KV tiles i, i-1, ..., 0); SYMMETRIC_SHIFT needs
+ *   ATTN_MASK_CAUSAL and an even tile count, else ATTN_ERR_UNSUPPORTED.
  *   workspace: device memory of at least attn_bwd_workspace_size(...) bytes,
  *   owned by the caller; contents need not be initialised and are scratch
  *   after the call. Concurrent calls must use distinct workspaces.

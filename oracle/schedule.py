@@ -18,7 +18,10 @@ the DASH pages describe, and the DAG they reason with:
   contributions one step after another. (§2.2 B, "Full Masks".) The pages'
   sequence i, i+1, ..., i-1 is read as the traversal of the other tile
   dimension by the worker owning a fixed KV tile, because §2.1 keeps all work
-  of one KV tile on one processor.
+  of one KV tile on one processor. On a causal mask (the English abstract of
+  the shd-paper.top digest credits Shift Scheduling for both masks) the same
+  cyclic walk leaves out the fully masked query tiles 0..j-1: worker j walks
+  j, ..., N-1, and dQ tile i receives KV tiles i, i-1, ..., 0 in step order.
 * Symmetric Shift (causal mask, N even): worker p owns KV tiles p and N-1-p.
   Phase 1 covers the dense lower-left rectangle (query tiles N/2..N-1 against
   KV tiles 0..N/2-1) with a cyclic shift; phase 2 covers the two remaining
@@ -107,10 +110,8 @@ def build(N: int, causal: bool, schedule: int) -> Plan:
             plan.workers.append([(s, i, j) for s, i in enumerate(q_tiles)])
         plan.orders = _kv_ascending_orders(N, causal)
     elif schedule == SHIFT:
-        if causal:
-            raise ValueError("Shift Scheduling as described covers the full mask")
         for j in range(N):
-            seq = list(range(j, N)) + list(range(0, j))
+            seq = [i for i in list(range(j, N)) + list(range(0, j)) if active(i, j, causal)]
             plan.workers.append([(s, i, j) for s, i in enumerate(seq)])
         plan.orders = _orders_by_step(N, plan.workers)
     elif schedule == SYMMETRIC_SHIFT:

@@ -29,7 +29,7 @@ def say(*a):
 
 def schedules(w, N):
     out = ["naive", "descending"]
-    out += ["symmetric_shift"] if (w.causal and N % 2 == 0) else ([] if w.causal else ["shift"])
+    out += ["shift"] + (["symmetric_shift"] if (w.causal and N % 2 == 0) else [])
     return out + [None]
 
 

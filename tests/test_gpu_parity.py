@@ -77,10 +77,8 @@ class Case:
 def schedules_for(S, D, causal, tile):
     T = dab.tile(S, D, tile)
     N = -(-S // T)
-    out = ["naive", "descending"]
-    if not causal:
-        out.append("shift")
-    elif N % 2 == 0:
+    out = ["naive", "descending", "shift"]
+    if causal and N % 2 == 0:
         out.append("symmetric_shift")
     return out + [None]
 
@@ -192,6 +190,6 @@ def test_wait_bound_reports_timeout():
 
 
 def test_rejects_unsupported_on_device():
-    c = Case(1, 1, 256, 64, True, 61)
+    c = Case(1, 1, 384, 64, True, 61)  # N = 3: Symmetric Shift needs an even tile count
     with pytest.raises(dab.AttnError):
-        dab.bwd(c.q, c.k, c.v, c.o, c.do, c.lse, True, "shift")
+        dab.bwd(c.q, c.k, c.v, c.o, c.do, c.lse, True, "symmetric_shift")

@@ -10,12 +10,15 @@ the weighted DAG (compute weight c, reduction weight r):
                 shift             : N(c+r)            (= the longest worker chain)
     causal      naive             : N(c+r) + (N-1) r
                 descending        : N(c+r)
+                shift             : N(c+r)
                 symmetric shift   : (N+1)(c+r) with N/2 workers of N+1 tasks each
 
 Derivation (naive, full): the reduction of task (q tile i, KV tile j) ends at
 E(i,j) = max(E(i-1,j) + c, E(i,j-1)) + r, whose solution is
 (i+1)(c+r) + j r. Descending, causal: E(i,j) = max(E(i+1,j) + c, E(i,j-1)) + r
-solves to (N-i)(c+r) + j r, largest at i = j = 0. Shift and Symmetric Shift
+solves to (N-i)(c+r) + j r, largest at i = j = 0. Shift, causal: the
+predecessor of (i, j) is (i, j+1), so E(i,j) = max(E(i-1,j) + c, E(i,j+1)) + r
+solves to (i-j+1)(c+r), largest at i = N-1, j = 0. Shift and Symmetric Shift
 never wait: each dQ tile's previous contribution finishes one step earlier.
 """
 
@@ -39,6 +42,7 @@ def cases():
         yield N, False, Sch.SHIFT
         yield N, True, Sch.NAIVE
         yield N, True, Sch.DESCENDING
+        yield N, True, Sch.SHIFT
         if N % 2 == 0:
             yield N, True, Sch.SYMMETRIC_SHIFT
 
@@ -104,6 +108,13 @@ def test_golden_shift():
     assert plan.orders == g["orders"]
 
 
+def test_golden_shift_causal():
+    g = json.load(open(os.path.join(GOLDEN, "shift_causal_n4.json")))
+    plan = Sch.build(g["N"], True, Sch.SHIFT)
+    assert [[i for _, i, _ in tasks] for tasks in plan.workers] == g["traversal"]
+    assert plan.orders == g["orders"]
+
+
 def test_golden_symmetric_shift():
     g = json.load(open(os.path.join(GOLDEN, "symmetric_shift_n4.json")))
     plan = Sch.build(g["N"], True, Sch.SYMMETRIC_SHIFT)
@@ -146,8 +157,6 @@ def test_cycle_is_detected():
 
 
 def test_invalid_requests():
-    with pytest.raises(ValueError):
-        Sch.build(4, True, Sch.SHIFT)
     with pytest.raises(ValueError):
         Sch.build(5, True, Sch.SYMMETRIC_SHIFT)
     with pytest.raises(ValueError):
