@@ -48,12 +48,17 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
         if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return ev
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
@@ -66,23 +71,31 @@ class HipEvents:
 
 
 def time_variant(fn, steps, warmup, torch, events, lib):
-    """Wall time of `steps` calls (synchronised both sides) and the mean main-kernel time."""
+    """Wall time of `steps` calls (synchronised both sides), the per-call API times
+    (HIP events around each whole call: pre-pass + main kernel + post-pass) and
+    the mean main-kernel time (events the library records around that launch)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
     pairs = [(events.create(), events.create()) for _ in range(steps)]
+    api = [(events.create(), events.create()) for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in pairs:
+    for (a, b), (c, d) in zip(pairs, api):
         lib.attn_set_timing_events(a, b)
+        events.record(c, stream)
         fn()
+        events.record(d, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     lib.attn_set_timing_events(None, None)
     kern = [events.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
+    api_ms = sorted(events.elapsed_ms(c, d) for c, d in api)
+    for a, b in pairs + api:
         events.destroy(a)
         events.destroy(b)
-    return wall / steps * 1e3, sum(kern) / len(kern)
+    q = lambda f: api_ms[min(len(api_ms) - 1, int(round(f * (len(api_ms) - 1))))]
+    return wall / steps * 1e3, sum(kern) / len(kern), {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
 
 
 KERNEL_SOURCES = ("bwd.hip", "common.hpp", "schedule.hpp", "launch.hpp")
@@ -143,6 +156,37 @@ def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
     }
 
 
+def rnd(x):
+    return {k: round(v, 4) for k, v in x.items()} if isinstance(x, dict) else round(x, 4)
+
+
+def wait_profile(w, sched, args, torch, dab, _lib, tensors):
+    """Fractions of wave time spent waiting, from one call of the profiling build (not timed)."""
+    q, k, v, o, do, lse = tensors
+    prof = _lib.load_profile()
+    saved = _lib._lib
+    try:
+        _lib._lib = prof
+        dab.set_dq_protocol(args.dq_protocol)
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, sched, w.tile)
+        for _ in range(2):
+            dab.bwd(q, k, v, o, do, lse, w.causal, sched, w.scale, w.tile, ws)
+        torch.cuda.synchronize()
+        buf = (ctypes.c_uint64 * (6 * 1024))()
+        n = prof.attn_debug_wait_profile(buf, 1024)
+        _lib.check(min(n, 0), "attn_debug_wait_profile")
+    finally:
+        _lib._lib = saved
+    rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
+    tot = [sum(r[j] for r in rows) for j in range(6)]
+    return {"schedule": sched, "workgroups": n,
+            "tile_waves_barrier_frac": round(tot[0] / max(tot[1], 1), 4),
+            "dq_waves_turn_wait_frac": round(tot[2] / max(tot[4], 1), 4),
+            "dq_waves_barrier_frac": round(tot[3] / max(tot[4], 1), 4),
+            "turn_wait_cycles_per_subtile": round(tot[2] / max(tot[5], 1), 1),
+            "note": "s_memtime cycles of one tile wave and one dQ wave per workgroup, profiling build"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +198,9 @@ def main():
     ap.add_argument("--dq-protocol", default="auto", choices=["auto", "device_atomic", "xcd_local"],
                     help="dQ hand-off of the deterministic calls (auto picks XCD-local where it applies)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle leg (0 = skip)")
+    ap.add_argument("--no-mfma-probe", action="store_true", help="skip the measured-MFMA-peak probe")
+    ap.add_argument("--wait-profile", action="store_true",
+                    help="one extra, untimed call of the best schedule with the profiling build: wait-cycle fractions")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -191,17 +238,17 @@ def main():
     for s in scheds:
         ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile)
         fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
-        ms, kms = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
         dab.check_workspace(ws)
-        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12}
+        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
         log(f"  {s:16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {results[s]['tflops']:7.1f} TFLOP/s")
         del ws
     nondet = None
     if not args.no_nondet:
         ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile)
         fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
-        ms, kms = time_variant(fn, args.steps, args.warmup, torch, events, lib)
-        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12}
+        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
         log(f"  {'atomic (non-det)':16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {nondet['tflops']:7.1f} TFLOP/s")
         del ws
 
@@ -214,7 +261,19 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {nbytes} bytes read + {nbytes} bytes written per copy, 3 copies")
 
+    mfma = None
+    if not args.no_mfma_probe:
+        tf, ghz = ctypes.c_double(), ctypes.c_double()
+        _lib.check(lib.attn_probe_mfma(200000, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                                       ctypes.byref(tf), ctypes.byref(ghz)), "attn_probe_mfma")
+        mfma = {"tflops": round(tf.value, 1), "sclk_ghz": round(ghz.value, 3),
+                "probe": "one workgroup per CU, 4 waves, 4 independent bf16 32x32x16 MFMA chains per wave"}
+        log(f"measured dense bf16 MFMA peak {tf.value:.1f} TFLOP/s at {ghz.value:.3f} GHz (s_memtime rate)")
     best = min(results, key=lambda s: results[s]["ms"])
+    wait = None
+    if args.wait_profile:
+        wait = wait_profile(w, best, args, torch, dab, _lib, (q, k, v, o, do, lse))
+        log(f"wait profile ({best}): {wait}")
     r = results[best]
     achieved = w.flops / (r["kernel_ms"] * 1e-3) / 1e12
     line = {
@@ -236,14 +295,18 @@ def main():
         "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
         "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,
         "schedules": {s: {"ms": round(v["ms"], 4), "kernel_ms": round(v["kernel_ms"], 4),
-                          "tflops": round(v["tflops"], 2)} for s, v in results.items()},
-        "nondet": {k2: round(v2, 4) for k2, v2 in nondet.items()} if nondet else None,
+                          "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"])} for s, v in results.items()},
+        "nondet": {k2: rnd(v2) for k2, v2 in nondet.items()} if nondet else None,
+        "mfma_measured": mfma,
+        "pct_measured_mfma_peak": round(100.0 * r["tflops"] / mfma["tflops"], 2) if mfma else None,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, best, args.dq_protocol),
                      "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
                      "kernel": "bwd_main_kernel", "kernel_ms": round(r["kernel_ms"], 4)},
     }
+    if wait is not None:
+        line["wait_profile"] = wait
     if args.cpu_seconds > 0:
         x_cpu = {n: x[n] for n in ("q", "k", "v", "do")}
         line["cpu_baseline"] = cpu_baseline(w, x_cpu, o.cpu(), lse.cpu(), args.cpu_seconds)

@@ -11,6 +11,7 @@ import os
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libattn_det.so")
+PROFILE_LIB_PATH = os.path.join(_PKG_DIR, "libattn_det_profile.so")
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -35,6 +36,8 @@ EXPORTS = (
     "attn_debug_set_wait_limit",
     "attn_set_timing_events",
     "attn_debug_set_dq_protocol",
+    "attn_probe_mfma",
+    "attn_debug_wait_profile",
 )
 
 _lib = None
@@ -51,11 +54,27 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+_profile_lib = None
+
+
+def load_profile() -> ctypes.CDLL:
+    """The profiling build (dQ-turn and barrier wait cycles); raises if it is missing."""
+    global _profile_lib
+    if _profile_lib is None:
+        _profile_lib = _open(PROFILE_LIB_PATH)
+    return _profile_lib
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m deterministic_attention_backward_amd.build` (needs hipcc)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -79,7 +98,10 @@ def load() -> ctypes.CDLL:
     lib.attn_set_timing_events.restype = None
     lib.attn_debug_set_dq_protocol.argtypes = [i]
     lib.attn_debug_set_dq_protocol.restype = i
-    _lib = lib
+    lib.attn_probe_mfma.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.attn_probe_mfma.restype = i
+    lib.attn_debug_wait_profile.argtypes = [ctypes.POINTER(ctypes.c_uint64), i]
+    lib.attn_debug_wait_profile.restype = i
     return lib
 
 

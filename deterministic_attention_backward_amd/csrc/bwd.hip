@@ -15,6 +15,7 @@
 // order: wait until the sub-tile's counter equals r(i, j), add, then (one
 // sub-tile later, when the adds have long completed) increment the counter. A
 // post-pass converts the fp32 accumulator to bf16 dq.
+#include "../../include/attn_det.h"
 #include "common.hpp"
 #include "launch.hpp"
 #include "schedule.hpp"
@@ -127,6 +128,26 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Profiling build (-DATTN_PROFILE_WAIT=1): per workgroup, the cycles the waves
+// spend waiting, read back with attn_debug_wait_profile:
+//   [0] tile waves at the two hand-over barriers  [1] tile waves in total
+//   [2] dQ waves waiting for their dQ turn         [3] dQ waves at the barriers
+//   [4] dQ waves in total                          [5] sub-tiles handed off
+#ifndef ATTN_PROFILE_WAIT
+#define ATTN_PROFILE_WAIT 0
+#endif
+constexpr bool kProfileWait = ATTN_PROFILE_WAIT != 0;
+__device__ unsigned long long g_wait_prof[kMaxGrid][6];
+static int g_last_grid = 0;
+
+struct WaitClock {
+  unsigned long long turn = 0, bar = 0;
+};
+__device__ __forceinline__ unsigned long long wclock() {
+  if constexpr (kProfileWait) return __builtin_amdgcn_s_memtime();
+  return 0;
+}
+
 // How a unit hands its dQ partials over.
 enum {
   MODE_ATOMIC = 0,  // non-deterministic: fp32 atomic adds in whatever order they land
@@ -206,6 +227,7 @@ struct TileRole {
   bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
   f32x16 s, dp;  // first row block of the current sub-tile, carried over barrier X
+  WaitClock* wc = nullptr;  // profiling build only
 
   __device__ __forceinline__ TileRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
     tid = threadIdx.x;
@@ -422,6 +444,7 @@ struct DqRole {
   u32x4 stq[GPT][4], sto[GPT][4];  // staged query sub-tile
   float stl = 0.0f, std_ = 0.0f;
   int pend = -1;  // counter whose increment this wave still owes
+  WaitClock* wc = nullptr;  // profiling build only
 
   __device__ __forceinline__ DqRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
     tb = threadIdx.x - G::NTA;
@@ -579,6 +602,7 @@ struct DqRole {
     if (ATOMIC || h_r == 0) return;
     // wait until every wave of the previous contributor has released
     const int target = G::NB * h_r;
+    const unsigned long long w0 = wclock();
     int seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t it = 0;
     while (__builtin_amdgcn_readfirstlane(seen) != target) {
@@ -589,6 +613,7 @@ struct DqRole {
       __builtin_amdgcn_s_sleep(2);
       seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if constexpr (kProfileWait) wc->turn += wclock() - w0;
     if (XCD) {
       // Every contributor of this tile runs on this XCD, so its L2 holds the
       // accumulator coherently for all of them: drop this CU's write-through
@@ -686,6 +711,10 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
     xq = (int)(x & (kMaxQueues - 1));
   }
   int* sUnit = L.unit();
+  WaitClock wclk;
+  if constexpr (kProfileWait) role.wc = &wclk;
+  const unsigned long long t_start = wclock();
+  unsigned long long n_sub = 0;
   for (;;) {
     lds_barrier();
     if (threadIdx.x == 0) {
@@ -765,12 +794,34 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       lds_barrier();
       for (int i = 0; i < sg.n; ++i) {
         role.part1(sg, i);
+        const unsigned long long b0 = wclock();
         lds_barrier();  // X
+        const unsigned long long b1 = wclock();
         role.part2(sg, i);
+        const unsigned long long b2 = wclock();
         lds_barrier();  // Y
+        if constexpr (kProfileWait) {
+          wclk.bar += (b1 - b0) + (wclock() - b2);
+          ++n_sub;
+        }
       }
       role.seg_end(sg);    // tile waves: park or write dK/dV; dQ waves: last sub-tile's dQ
       t0 = t1;
+    }
+  }
+  if constexpr (kProfileWait) {
+    const unsigned long long total = wclock() - t_start;
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < kMaxGrid) {
+      if (wave == 0) {
+        g_wait_prof[blockIdx.x][0] = wclk.bar;
+        g_wait_prof[blockIdx.x][1] = total;
+      } else if (wave == G::NA) {
+        g_wait_prof[blockIdx.x][2] = wclk.turn;
+        g_wait_prof[blockIdx.x][3] = wclk.bar;
+        g_wait_prof[blockIdx.x][4] = total;
+        g_wait_prof[blockIdx.x][5] = n_sub;
+      }
     }
   }
 }
@@ -829,6 +880,7 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
 
 template <int D, int T, int BR, bool CAUSAL, int MODE>
 static hipError_t launch_main(const MainParams& mp, int grid, hipStream_t stream) {
+  g_last_grid = grid;
   hipLaunchKernelGGL((bwd_main_kernel<D, T, BR, CAUSAL, MODE>), dim3((unsigned)grid), dim3(T / 16 * 64), 0, stream,
                      mp);
   return hipGetLastError();
@@ -963,3 +1015,15 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
 }
 
 }  // namespace attn
+
+extern "C" int attn_debug_wait_profile(uint64_t* out, int max_workgroups) {
+  if (!attn::kProfileWait) return ATTN_ERR_UNSUPPORTED;
+  if (!out || max_workgroups <= 0) return ATTN_ERR_INVALID_ARG;
+  static unsigned long long rows[attn::kMaxGrid][6];
+  if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
+  if (hipMemcpyFromSymbol(rows, HIP_SYMBOL(attn::g_wait_prof), sizeof(rows)) != hipSuccess) return ATTN_ERR_HIP;
+  const int n = attn::g_last_grid < max_workgroups ? attn::g_last_grid : max_workgroups;
+  for (int g = 0; g < n; ++g)
+    for (int k = 0; k < 6; ++k) out[6 * g + k] = rows[g][k];
+  return n;
+}

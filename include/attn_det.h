@@ -185,6 +185,30 @@ int attn_debug_set_dq_protocol(int protocol);
  */
 void attn_set_timing_events(void* before, void* after);
 
+/*
+ * attn_probe_mfma - measurement probe (not part of the backward): runs one
+ * workgroup per CU that issues `iterations` x 4 independent bf16
+ * v_mfma_f32_32x32x16 per wave (one wave per SIMD), after one warm-up launch,
+ * on `stream` (a hipStream_t), and waits for it. *tflops receives the dense
+ * bf16 MFMA throughput reached; *ghz the rate of the shader clock counter
+ * (s_memtime) over the timed launch, i.e. the clock the matrix cores ran at.
+ * Uses a small static device array; no allocation. Not thread-safe.
+ */
+int attn_probe_mfma(int iterations, void* stream, double* tflops, double* ghz);
+
+/*
+ * attn_debug_wait_profile - only in the profiling build of the library
+ * (libattn_det_profile.so, compiled with ATTN_PROFILE_WAIT=1); the regular
+ * build returns ATTN_ERR_UNSUPPORTED. Synchronises the device, then writes,
+ * for each workgroup of the last backward launch (at most max_workgroups),
+ * six uint64 values: tile-wave cycles at the two per-sub-tile hand-over
+ * barriers, tile-wave total cycles, dQ-wave cycles waiting for their dQ turn,
+ * dQ-wave cycles at the barriers, dQ-wave total cycles, sub-tiles processed
+ * (cycles of the s_memtime counter, one wave of each kind). Returns the
+ * number of workgroups written (>= 0) or a negative status.
+ */
+int attn_debug_wait_profile(uint64_t* out, int max_workgroups);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,55 @@
+"""GPU checks of the measurement helpers: the MFMA probe and the profiling build.
+
+The profiling build (ATTN_PROFILE_WAIT=1) only adds clock reads around waits,
+so its gradients must be bit-identical to the regular library's.
+"""
+
+import ctypes
+
+import pytest
+import torch
+
+import attn_inputs
+import deterministic_attention_backward_amd as dab
+from deterministic_attention_backward_amd import _lib
+
+pytestmark = pytest.mark.gpu
+
+
+def test_mfma_probe_is_plausible():
+    lib = _lib.load()
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    st = lib.attn_probe_mfma(20000, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                             ctypes.byref(tf), ctypes.byref(ghz))
+    assert st == 0
+    print(f"probe: {tf.value:.1f} TFLOP/s at {ghz.value:.3f} GHz", flush=True)
+    # dense bf16 peak of the part is about 2.5 PFLOP/s at 2.4 GHz
+    assert 100.0 < tf.value < 3000.0
+    assert 0.3 < ghz.value < 3.5
+    assert lib.attn_debug_wait_profile((ctypes.c_uint64 * 6)(), 1) == _lib.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("causal,sched", [(False, "shift"), (True, "symmetric_shift"), (True, "naive")])
+def test_profiling_build_is_bitwise_identical(causal, sched):
+    B, H, S, D = 1, 4, 1024, 128
+    x = attn_inputs.draw(B, H, S, D, 71)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = dab.fwd(q, k, v, causal)
+    ref = dab.bwd(q, k, v, o, do, lse, causal, sched)
+    torch.cuda.synchronize()
+    prof = _lib.load_profile()
+    saved = _lib._lib
+    try:
+        _lib._lib = prof
+        got = dab.bwd(q, k, v, o, do, lse, causal, sched)
+        torch.cuda.synchronize()
+        buf = (ctypes.c_uint64 * (6 * 1024))()
+        n = prof.attn_debug_wait_profile(buf, 1024)
+    finally:
+        _lib._lib = saved
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert n > 0
+    rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
+    assert sum(r[5] for r in rows) > 0            # sub-tiles were counted
+    assert all(r[2] <= r[4] and r[0] <= r[1] for r in rows)  # waits are part of the total
