@@ -188,7 +188,7 @@ struct Geo {
   static constexpr int LDS_BYTES = UNIT_OFF + 16;
   static_assert(QBW >= 1 && QBW * NB == MB * ND && QBW <= ND && ND % QBW == 0, "dQ block split");
   static_assert(GPT >= 1 && GROUPS % NTB == 0 && T % BR == 0 && BR <= NTB, "staging split");
-  static_assert(D * TP * 2 <= TR_BYTES, "K^T must fit the transposed staging area");
+  static_assert(T * DP * 2 <= TR_BYTES, "the K rows must fit the transposed staging area");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -269,13 +269,10 @@ struct TileRole {
       if constexpr (VL) *(bf16x8*)&L.v()[(32 * a + l32) * G::DP + 16 * c + 8 * hh] = vv;
       else Vr[VL ? 0 : c] = vv;
     }
-    // K^T for the dQ waves' operand
+    // K rows for the dQ waves' operand (they read it transposed)
     bf16* kt = L.kt();
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kt[(16 * c + 8 * hh + e) * G::TP + 32 * a + l32] = Kr[c][e];
-    }
+    for (int c = 0; c < KC; ++c) *(bf16x8*)&kt[(32 * a + l32) * G::DP + 16 * c + 8 * hh] = Kr[c];
     if (sg.restore) {
       park(sg, true);
     } else {
@@ -549,12 +546,18 @@ struct DqRole {
   __device__ __forceinline__ void seg_begin(const Seg& sg) { stage_load(sg.bh, sub_row0(sg, 0)); }
 
   __device__ __forceinline__ void seg_kd(const Seg&) {
+    // K^T columns through the transpose read from the row-major K rows: lane i
+    // of a 16-lane group gets four consecutive keys of feature column cb + i
     const bf16* kt = L.kt();
+    const int grp = lane >> 4, gi = lane & 15;
 #pragma unroll
     for (int j = 0; j < QBW; ++j) {
+      const int cb = 32 * (nb0 + j) + 16 * (grp & 1) + 4 * (gi & 3);
 #pragma unroll
-      for (int c = 0; c < TC; ++c)
-        Kd[j][c] = *(const bf16x8*)&kt[(32 * (nb0 + j) + l32) * G::TP + 16 * c + 8 * hh];
+      for (int c = 0; c < TC; ++c) {
+        const bf16* r0 = &kt[(16 * c + 8 * (grp >> 1) + (gi >> 2)) * G::DP + cb];
+        Kd[j][c] = cat44(lds_read_tr(r0), lds_read_tr(r0 + 4 * G::DP));
+      }
     }
   }
 
