@@ -193,3 +193,24 @@ def test_rejects_unsupported_on_device():
     c = Case(1, 1, 384, 64, True, 61)  # N = 3: Symmetric Shift needs an even tile count
     with pytest.raises(dab.AttnError):
         dab.bwd(c.q, c.k, c.v, c.o, c.do, c.lse, True, "symmetric_shift")
+
+
+@pytest.mark.parametrize("sched", ["naive", "shift"])
+def test_workspace_reuse_sees_fresh_accumulators(sched):
+    # One workspace, many calls with different inputs: every call's dQ must match
+    # the atomic variant's on the same inputs (a running sum left in a cache by an
+    # earlier call, or by an earlier contributor, would show up as a large error).
+    B, H, S, D = 2, 8, 2048, 128
+    ws = dab.alloc_workspace(B, H, S, D, False, sched)
+    for seed in range(80, 86):
+        x = attn_inputs.draw(B, H, S, D, seed)
+        q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+        o, lse = dab.fwd(q, k, v, False)
+        say(f"workspace reuse: schedule={sched} seed={seed}")
+        dq, dk, dv = dab.bwd(q, k, v, o, do, lse, False, sched, workspace=ws)
+        dab.check_workspace(ws)
+        rq, rk, rv = dab.bwd_nondeterministic(q, k, v, o, do, lse, False)
+        torch.cuda.synchronize()
+        for name, a, b in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            err = (a.float() - b.float()).abs().max().item()
+            assert err <= 2e-2, f"{sched} seed {seed} {name}: {err:.3e}"
