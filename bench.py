@@ -235,13 +235,17 @@ def main():
         scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else [])
     out = tuple(torch.empty_like(q) for _ in range(3))
     results = {}
+    dab.wait_timeouts(reset=True)
     for s in scheds:
         ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile)
         fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
         ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
         dab.check_workspace(ws)
-        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
+        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api,
+                      "wait_timeouts": dab.wait_timeouts(reset=True)}
         log(f"  {s:16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {results[s]['tflops']:7.1f} TFLOP/s")
+        if results[s]["wait_timeouts"]:
+            log(f"  WARNING: {results[s]['wait_timeouts']} bounded dQ waits ran out during the {s} calls")
         del ws
     nondet = None
     if not args.no_nondet:
@@ -295,7 +299,9 @@ def main():
         "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
         "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,
         "schedules": {s: {"ms": round(v["ms"], 4), "kernel_ms": round(v["kernel_ms"], 4),
-                          "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"])} for s, v in results.items()},
+                          "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"]),
+                          "wait_timeouts": v["wait_timeouts"]} for s, v in results.items()},
+        "dq_wait_timeouts": sum(v["wait_timeouts"] for v in results.values()),
         "nondet": {k2: rnd(v2) for k2, v2 in nondet.items()} if nondet else None,
         "mfma_measured": mfma,
         "pct_measured_mfma_peak": round(100.0 * r["tflops"] / mfma["tflops"], 2) if mfma else None,

@@ -182,3 +182,10 @@ def set_dq_protocol(protocol="auto") -> None:
 def set_wait_limit(iterations: int = 0, poison: bool = False) -> None:
     """Debug: bound on one dQ ordering wait (0 = default) and counter poisoning for the next calls."""
     _lib.load().attn_debug_set_wait_limit(int(iterations), 1 if poison else 0)
+
+
+def wait_timeouts(reset: bool = True) -> int:
+    """Synchronise the device; bounded waits that ran out since the last reset, in any call of this process."""
+    n = _lib.load().attn_debug_wait_timeouts(1 if reset else 0)
+    _lib.check(n if n < 0 else 0, "attn_debug_wait_timeouts")
+    return n

@@ -38,6 +38,7 @@ EXPORTS = (
     "attn_debug_set_dq_protocol",
     "attn_probe_mfma",
     "attn_debug_wait_profile",
+    "attn_debug_wait_timeouts",
 )
 
 _lib = None
@@ -102,6 +103,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.attn_probe_mfma.restype = i
     lib.attn_debug_wait_profile.argtypes = [ctypes.POINTER(ctypes.c_uint64), i]
     lib.attn_debug_wait_profile.restype = i
+    lib.attn_debug_wait_timeouts.argtypes = [i]
+    lib.attn_debug_wait_timeouts.restype = i
     return lib
 
 

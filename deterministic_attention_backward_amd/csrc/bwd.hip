@@ -38,12 +38,39 @@ struct PreParams {
   int poison;
 };
 
+// Control-word accesses: atomic read-modify-writes at device scope only.
+__device__ __forceinline__ void ctl_set(int* w, int v) {
+  (void)__hip_atomic_exchange(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ctl_read(int* w) {
+  return __hip_atomic_fetch_add(w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Number of bounded waits that ran out since the last read (all launches of
+// this process on this device); read and cleared by attn_debug_wait_timeouts.
+__device__ int g_wait_timeouts;
+
+__device__ __forceinline__ void note_timeout(int* header) {
+  ctl_set(&header[1], 1);
+  atomicAdd(&g_wait_timeouts, 1);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
   constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
   const int sub = threadIdx.x % LPR;
+  // Control words (dQ turn counters, tickets, head table) are only ever touched
+  // by atomic read-modify-writes, here and in the main kernel, so every access
+  // to them is performed at the same place in the memory hierarchy whatever
+  // cache a line may still sit in. Every counter starts at 0; the optional
+  // poison value (an unreachable turn, used to exercise the wait bound) is
+  // written by the thread that owns that slot.
+  for (long long i = gtid; i < p.n_counters; i += nthreads)
+    ctl_set(&p.counters[i], (p.poison && i == p.n_counters - 1) ? 0x40000000 : 0);
+  if (gtid < 64) ctl_set(&p.header[gtid], 0);
+  for (long long i = gtid; i < p.n_heads; i += nthreads) ctl_set(&p.heads[i], -1);
   for (long long base = gtid / LPR; base < p.rows; base += nthreads / LPR) {
     const long long bh = base / p.S_pad;
     const int s = (int)(base % p.S_pad);
@@ -63,12 +90,6 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
       p.lse2[base] = (s < p.S) ? p.lse[bh * p.S + s] * 1.4426950408889634f : __builtin_inff();
     }
   }
-  // every counter starts at 0; the optional poison value (an unreachable turn,
-  // used to exercise the wait bound) is written by the thread that owns that slot
-  for (long long i = gtid; i < p.n_counters; i += nthreads)
-    p.counters[i] = (p.poison && i == p.n_counters - 1) ? 0x40000000 : 0;
-  if (gtid < 64) p.header[gtid] = 0;
-  for (long long i = gtid; i < p.n_heads; i += nthreads) p.heads[i] = -1;
   for (long long i = gtid * 4; i < p.dq_ws_elems; i += nthreads * 4)
     *(f32x4*)(p.dq_ws + i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
@@ -535,6 +556,13 @@ struct DqRole {
       dsA[c] = cat44(lds_read_tr(base + 16 * c * G::SP), lds_read_tr(base + (16 * c + 4) * G::SP));
   }
 
+  // the counter as one wave-uniform value: lane 0 reads it, the wave shares it
+  __device__ __forceinline__ int turn_read(int* cnt) const {
+    int v = 0;
+    if (lane == 0) v = ctl_read(cnt);
+    return __builtin_amdgcn_readfirstlane(v);
+  }
+
   __device__ __forceinline__ void release() {
     if (!ATOMIC && pend >= 0) {
       wait_vmem();  // this wave's dQ updates have completed
@@ -606,15 +634,16 @@ struct DqRole {
     // wait until every wave of the previous contributor has released
     const int target = G::NB * h_r;
     const unsigned long long w0 = wclock();
-    int seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int* const cnt = &p.counters[h_cidx];
+    int seen = turn_read(cnt);
     uint32_t it = 0;
-    while (__builtin_amdgcn_readfirstlane(seen) != target) {
+    while (seen != target) {
       if (++it >= p.wait_limit) {
-        __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) note_timeout(p.header);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
-      seen = __hip_atomic_load(&p.counters[h_cidx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      seen = turn_read(cnt);
     }
     if constexpr (kProfileWait) wc->turn += wclock() - w0;
     if (XCD) {
@@ -737,12 +766,12 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
           int* slot = &p.heads[xq * p.BH + i];
           if (wk == 0) {
             head = min(atomicAdd(&p.header[2], 1), p.BH);
-            __hip_atomic_store(slot, head, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ctl_set(slot, head);
           } else {
             uint32_t it = 0;
-            while ((head = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < 0) {
+            while ((head = ctl_read(slot)) < 0) {
               if (++it >= p.wait_limit) {
-                __hip_atomic_store(&p.header[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                note_timeout(p.header);
                 head = p.BH;
                 break;
               }
@@ -1028,5 +1057,16 @@ extern "C" int attn_debug_wait_profile(uint64_t* out, int max_workgroups) {
   const int n = attn::g_last_grid < max_workgroups ? attn::g_last_grid : max_workgroups;
   for (int g = 0; g < n; ++g)
     for (int k = 0; k < 6; ++k) out[6 * g + k] = rows[g][k];
+  return n;
+}
+
+extern "C" int attn_debug_wait_timeouts(int reset) {
+  if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
+  int n = 0;
+  if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(attn::g_wait_timeouts), sizeof(n)) != hipSuccess) return ATTN_ERR_HIP;
+  if (reset) {
+    const int zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(attn::g_wait_timeouts), &zero, sizeof(zero)) != hipSuccess) return ATTN_ERR_HIP;
+  }
   return n;
 }

@@ -161,6 +161,16 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
 
 /*
+ * attn_debug_wait_timeouts - synchronises the current device, then returns how
+ * many bounded waits (dQ turns and head claims) ran out since the count was
+ * last cleared, over every backward launch of this process on that device
+ * (>= 0), or a negative status. Unlike attn_bwd_check this is not tied to one
+ * workspace or to the last call. reset != 0 clears the count after reading.
+ * Host-blocking; for tests and benchmarks.
+ */
+int attn_debug_wait_timeouts(int reset);
+
+/*
  * attn_debug_set_dq_protocol - how deterministic calls hand dQ partials over
  * (the order is the schedule's in every case):
  *   0 (default) choose per call: XCD-local when every worker of a head can be

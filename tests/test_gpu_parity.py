@@ -169,12 +169,14 @@ def test_forward_bitwise_reproducible():
         assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32))
 
 
+@pytest.mark.expects_timeout
 def test_wait_bound_reports_timeout():
     # a poisoned counter can never reach its turn; the bounded wait must give up,
     # record the timeout and let every workgroup finish normally
     c = Case(1, 2, 512, 64, False, 51)
     ws = dab.alloc_workspace(1, 2, 512, 64, False, "naive", 0)
     say("timeout path: poisoned counter, wait bound 2000 iterations")
+    dab.wait_timeouts(reset=True)
     try:
         dab.set_wait_limit(2000, poison=True)
         dab.bwd(c.q, c.k, c.v, c.o, c.do, c.lse, False, "naive", workspace=ws)
@@ -183,8 +185,11 @@ def test_wait_bound_reports_timeout():
         assert err.value.status == -6
     finally:
         dab.set_wait_limit(0, poison=False)
+    # the process-wide count saw it too (one dQ wave per expired wait and workgroup)
+    assert dab.wait_timeouts(reset=True) >= 1
     # the next call is clean again
     dq, dk, dv = c.run("naive")
+    assert dab.wait_timeouts(reset=False) == 0
     dq_r, dk_r, dv_r = c.ref()
     assert_close("dQ after timeout", f64(dq), dq_r)
 
