@@ -180,7 +180,7 @@ def set_dq_protocol(protocol="auto") -> None:
 
 
 def set_wait_limit(iterations: int = 0, poison: bool = False) -> None:
-    """Debug: bound on one dQ ordering wait (0 = default) and counter poisoning for the next calls."""
+    """Debug: bound on one dQ ordering wait (0 = default) and flag poisoning for the next calls."""
     _lib.load().attn_debug_set_wait_limit(int(iterations), 1 if poison else 0)
 
 

@@ -14,7 +14,7 @@ using namespace attn;
 
 namespace {
 
-constexpr uint32_t kDefaultWaitLimit = 1u << 24;
+constexpr uint32_t kDefaultWaitLimit = 1u << 21;
 uint32_t g_wait_limit = kDefaultWaitLimit;
 int g_poison = 0;
 int g_dq_protocol = DQ_AUTO;
@@ -50,7 +50,8 @@ int check_shape(int B, int H, int S, int D, int mask, int schedule, int tile_req
   const long long BH = static_cast<long long>(B) * H;
   const int BR = bwd_sub_rows(D, T);
   // index arithmetic on the device uses 32-bit unit and counter indices
-  if (BH * N * (T / BR) >= (1ll << 31) || BH * N * T * D >= (1ll << 40)) return ATTN_ERR_UNSUPPORTED;
+  if (BH * align64(N * (T / BR) * dq_waves(T)) >= (1ll << 31) || BH * N * T * D >= (1ll << 40))
+    return ATTN_ERR_UNSUPPORTED;
   if (deterministic) {
     if (schedule == ATTN_SCHED_SYMMETRIC_SHIFT && (mask != ATTN_MASK_CAUSAL || (N % 2) != 0))
       return ATTN_ERR_UNSUPPORTED;

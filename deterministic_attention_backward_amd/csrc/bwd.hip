@@ -23,27 +23,34 @@
 namespace attn {
 
 // --------------------------------------------------------------------------------------
-// pre-pass: Delta = rowsum(dO * O) in fp32, LSE in base 2, counters and ticket reset.
+// pre-pass: Delta = rowsum(dO * O) in fp32, LSE in base 2, hand-off flags and tickets reset.
 
 struct PreParams {
   const bf16 *o, *dout;
   const float* lse;
   float *lse2, *delta, *dq_ws;
-  int *counters, *header, *heads;
+  int *flags, *header, *heads;
   long long n_heads;    // entries of the head table
   long long rows;       // BH * S_pad
   int S, S_pad;
-  long long n_counters;
+  long long n_flags;
   long long dq_ws_elems;  // > 0: zero the dQ accumulator (atomic variant)
-  int poison;
 };
 
-// Control-word accesses: atomic read-modify-writes at device scope only.
+// Control words shared between XCDs (tickets, head claims, the hand-off flags of
+// the cross-XCD protocol) are only touched by atomic read-modify-writes at
+// device scope, so every access meets the others at the same place. A read is
+// an atomic OR with a zero the compiler cannot see: an RMW whose operand is a
+// known identity (add 0, or 0) is folded into an atomic load, which the cache
+// hierarchy serves like any other load and which then need not observe the
+// RMWs other waves perform on the word.
 __device__ __forceinline__ void ctl_set(int* w, int v) {
   (void)__hip_atomic_exchange(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ctl_read(int* w) {
-  return __hip_atomic_fetch_add(w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return __hip_atomic_fetch_or(w, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Number of bounded waits that ran out since the last read (all launches of
@@ -61,14 +68,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
   const long long gtid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
   const int sub = threadIdx.x % LPR;
-  // Control words (dQ turn counters, tickets, head table) are only ever touched
-  // by atomic read-modify-writes, here and in the main kernel, so every access
-  // to them is performed at the same place in the memory hierarchy whatever
-  // cache a line may still sit in. Every counter starts at 0; the optional
-  // poison value (an unreachable turn, used to exercise the wait bound) is
-  // written by the thread that owns that slot.
-  for (long long i = gtid; i < p.n_counters; i += nthreads)
-    ctl_set(&p.counters[i], (p.poison && i == p.n_counters - 1) ? 0x40000000 : 0);
+  // Control words (hand-off flags, tickets, head table) start at 0 (head slots at
+  // -1). The main kernel launches after this kernel has completed, which makes
+  // these values visible to every XCD.
+  for (long long i = gtid; i < p.n_flags; i += nthreads) ctl_set(&p.flags[i], 0);
   if (gtid < 64) ctl_set(&p.header[gtid], 0);
   for (long long i = gtid; i < p.n_heads; i += nthreads) ctl_set(&p.heads[i], -1);
   for (long long base = gtid / LPR; base < p.rows; base += nthreads / LPR) {
@@ -121,11 +124,34 @@ struct MainParams {
   const float *lse2, *delta;
   float *dq_ws, *park;
   bf16* dq;
-  int *counters, *header, *heads;
+  int *flags, *header, *heads;
   int S, S_pad, N, n_qsub, n_workers, n_units, sched, BH;
+  int flag_stride, heads_row;  // int32 elements per head of flags / per queue row of heads
+  int poison_flag;             // >= 0: the wait on this flag can never succeed (exercises the bound)
   float scale, scale_log2;
   uint32_t wait_limit;
 };
+
+// XCD-local words (hand-off flags, head slots, the dQ accumulator): plain
+// stores, which pass the CU's write-through L1 and land in the XCD's L2, and
+// agent-scope loads, which skip the L1 and are served by that L2. Every access
+// of such a word within a launch comes from one XCD, so its L2 is the single
+// place where they all meet. (A plain load may be served by a stale L1 line,
+// and an L1 invalidate at workgroup scope does not drop it.)
+__device__ __forceinline__ void l2_store(int* w, int v) {
+  asm volatile("" ::: "memory");
+  *w = v;
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ int l2_load(int* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at base + byte_off through a buffer resource (base wave-uniform,
+// byte_off < bytes), as an agent-scope load served by the XCD's L2.
+__device__ __forceinline__ f32x4 l2_load16(const float* base, unsigned bytes, unsigned byte_off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */));
+}
 
 // Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // supplies the address of a 4-element row chunk and receives element i % 4 of
@@ -172,7 +198,7 @@ __device__ __forceinline__ unsigned long long wclock() {
 // How a unit hands its dQ partials over.
 enum {
   MODE_ATOMIC = 0,  // non-deterministic: fp32 atomic adds in whatever order they land
-  MODE_DEVICE = 1,  // deterministic: device-scope atomic RMWs serialised by the counters
+  MODE_DEVICE = 1,  // deterministic: device-scope atomic RMWs serialised by the hand-off flags
   MODE_XCD = 2      // deterministic: all workers of a head on one XCD, plain RMW via its L2
 };
 
@@ -461,7 +487,8 @@ struct DqRole {
   bf16x8 dsA[TC];       // A operand of dQ: dS rows of this wave's row block
   u32x4 stq[GPT][4], sto[GPT][4];  // staged query sub-tile
   float stl = 0.0f, std_ = 0.0f;
-  int pend = -1;  // counter whose increment this wave still owes
+  int pend = -1;      // flag this wave still owes a hand-over on
+  int pend_val = 0;   // the value it will write there
   WaitClock* wc = nullptr;  // profiling build only
 
   __device__ __forceinline__ DqRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
@@ -556,17 +583,28 @@ struct DqRole {
       dsA[c] = cat44(lds_read_tr(base + 16 * c * G::SP), lds_read_tr(base + (16 * c + 4) * G::SP));
   }
 
-  // the counter as one wave-uniform value: lane 0 reads it, the wave shares it
-  __device__ __forceinline__ int turn_read(int* cnt) const {
+  // A hand-off flag as one wave-uniform value. XCD-local: every contributor of
+  // the tile runs on this XCD, so its L2 holds the flag; across XCDs: an atomic
+  // read-modify-write.
+  __device__ __forceinline__ int flag_read(int* f) const {
     int v = 0;
-    if (lane == 0) v = ctl_read(cnt);
+    if (XCD) {
+      v = l2_load(f);
+    } else if (lane == 0) {
+      v = ctl_read(f);
+    }
     return __builtin_amdgcn_readfirstlane(v);
   }
 
+  // Once every dQ update this wave issued has completed, tell the next
+  // contributor of the same blocks that it may go ahead.
   __device__ __forceinline__ void release() {
     if (!ATOMIC && pend >= 0) {
-      wait_vmem();  // this wave's dQ updates have completed
-      if (lane == 0) __hip_atomic_fetch_add(&p.counters[pend], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (lane == 0) {
+        if (XCD) l2_store(&p.flags[pend], pend_val);
+        else ctl_set(&p.flags[pend], pend_val);
+      }
       pend = -1;
     }
   }
@@ -603,7 +641,7 @@ struct DqRole {
   //   release (next interval):    once the stores have completed, count this
   //            wave's contribution on the sub-tile's counter.
   f32x16 acc[QBW], prev[QBW];
-  int h_cidx = 0, h_r = 0;
+  int h_flag = 0, h_r = 0;
   bool h_last = true;
   float* h_row = nullptr;
 
@@ -626,16 +664,19 @@ struct DqRole {
       for (int c = 0; c < TC; ++c) acc[x] = mfma32(dsA[c], Kd[x][c], acc[x]);
     }
     const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + j / NSUB);
-    h_cidx = sg.bh * p.n_qsub + t.q * NSUB + j % NSUB;
+    // this wave's flag for the sub-tile: dQ wave b of every contributor updates
+    // the same blocks of the accumulator, so it waits only for wave b of the
+    // previous contributor
+    h_flag = sg.bh * p.flag_stride + (t.q * NSUB + j % NSUB) * G::NB + b;
     h_r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, t.q, sg.kv);
     h_last = ATOMIC ? true : (h_r == sched_contributors(p.N, CAUSAL, t.q) - 1);
     h_row = p.dq_ws + ((size_t)sg.bh * p.S_pad + t.q * G::T + (j % NSUB) * BR) * D;  // uniform
     if (ATOMIC || h_r == 0) return;
-    // wait until every wave of the previous contributor has released
-    const int target = G::NB * h_r;
+    // wait until the previous contributor's wave b has handed over (flag == r)
+    const int target = h_r + (h_flag == p.poison_flag ? 0x40000000 : 0);
     const unsigned long long w0 = wclock();
-    int* const cnt = &p.counters[h_cidx];
-    int seen = turn_read(cnt);
+    int* const fl = &p.flags[h_flag];
+    int seen = flag_read(fl);
     uint32_t it = 0;
     while (seen != target) {
       if (++it >= p.wait_limit) {
@@ -643,19 +684,17 @@ struct DqRole {
         break;
       }
       __builtin_amdgcn_s_sleep(2);
-      seen = turn_read(cnt);
+      seen = flag_read(fl);
     }
     if constexpr (kProfileWait) wc->turn += wclock() - w0;
     if (XCD) {
       // Every contributor of this tile runs on this XCD, so its L2 holds the
-      // accumulator coherently for all of them: drop this CU's write-through
-      // L1 copies, then read the running sum.
-      asm volatile("buffer_inv sc0" ::: "memory");
+      // accumulator coherently for all of them: read the running sum there.
 #pragma unroll
       for (int x = 0; x < QBW; ++x) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 v = *at_bytes((const f32x4*)h_row, quad_off(x, g));
+          const f32x4 v = l2_load16(h_row, 4u * BR * D, quad_off(x, g));
 #pragma unroll
           for (int k = 0; k < 4; ++k) prev[x][4 * g + k] = v[k];
         }
@@ -685,7 +724,7 @@ struct DqRole {
         }
       }
     } else {
-      // Device-scope atomic RMWs, serialised by the counters: each element
+      // Device-scope atomic RMWs, serialised by the hand-off flags: each element
       // receives the same fp32 additions in the same order on every run; the
       // first contributor swaps its value in.
 #pragma unroll
@@ -701,7 +740,10 @@ struct DqRole {
         }
       }
     }
-    if (!h_last) pend = h_cidx;
+    if (!h_last) {
+      pend = h_flag;
+      pend_val = h_r + 1;
+    }
   }
 
   __device__ __forceinline__ void part1(const Seg& sg, int i) {
@@ -756,20 +798,21 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
         sUnit[1] = u % p.n_workers;
       } else {
         // Units of one head are consecutive tickets of one XCD's queue; the
-        // ticket of a head's first worker claims the next unclaimed head and
-        // publishes it for the others (lower tickets are held by running
-        // workgroups, so the wait below always ends).
+        // ticket of a head's first worker claims the next unclaimed head (an
+        // atomic shared by all XCDs) and publishes it for the others through
+        // this XCD's L2 (lower tickets are held by running workgroups, so the
+        // wait below always ends).
         const int k = atomicAdd(&p.header[16 + xq], 1);
         const int i = k / p.n_workers, wk = k % p.n_workers;
         int head = p.BH;
         if (i < p.BH) {
-          int* slot = &p.heads[xq * p.BH + i];
+          int* slot = &p.heads[xq * p.heads_row + i];
           if (wk == 0) {
             head = min(atomicAdd(&p.header[2], 1), p.BH);
-            ctl_set(slot, head);
+            l2_store(slot, head);
           } else {
             uint32_t it = 0;
-            while ((head = ctl_read(slot)) < 0) {
+            while ((head = l2_load(slot)) < 0) {
               if (++it >= p.wait_limit) {
                 note_timeout(p.header);
                 head = p.BH;
@@ -955,7 +998,7 @@ static hipError_t dispatch_mask(const MainParams& mp, bool causal, bool atomic, 
 hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   const long long BH = (long long)a.B * a.H;
   int* header = (int*)(a.ws + a.lay.header);
-  int* counters = (int*)(a.ws + a.lay.counters);
+  int* flags = (int*)(a.ws + a.lay.flags);
   float* lse2 = (float*)(a.ws + a.lay.lse2);
   float* delta = (float*)(a.ws + a.lay.delta);
   float* dq_ws = (float*)(a.ws + a.lay.dq_ws);
@@ -969,16 +1012,15 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   pp.lse2 = lse2;
   pp.delta = delta;
   pp.dq_ws = dq_ws;
-  pp.counters = counters;
+  pp.flags = flags;
   pp.header = header;
   pp.heads = heads;
-  pp.n_heads = (long long)kMaxQueues * BH;
+  pp.n_heads = (long long)kMaxQueues * a.lay.heads_row;
   pp.rows = BH * a.S_pad;
   pp.S = a.S;
   pp.S_pad = a.S_pad;
-  pp.n_counters = BH * a.n_qsub;
+  pp.n_flags = BH * a.lay.flag_stride;
   pp.dq_ws_elems = a.atomic ? BH * a.S_pad * a.D : 0;
-  pp.poison = a.atomic ? 0 : a.poison;
   {
     const long long want = (pp.rows * (a.D / 8) + 255) / 256;
     const unsigned grid = (unsigned)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
@@ -999,7 +1041,11 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.delta = delta;
   mp.dq_ws = dq_ws;
   mp.park = park;
-  mp.counters = counters;
+  mp.flags = flags;
+  mp.flag_stride = (int)a.lay.flag_stride;
+  mp.heads_row = (int)a.lay.heads_row;
+  // poisoning: the last dQ wave's flag of the last query sub-tile of the last head
+  mp.poison_flag = (!a.atomic && a.poison) ? (int)((BH - 1) * a.lay.flag_stride + (long long)a.n_qsub * dq_waves(a.T) - 1) : -1;
   mp.header = header;
   mp.heads = heads;
   mp.dq = (bf16*)a.dq;

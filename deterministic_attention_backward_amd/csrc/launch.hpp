@@ -22,23 +22,34 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Byte layout of the backward workspace (every region 256-byte aligned):
 //   header   int32[64]: [0] unit ticket, [1] timeout flag, [2] next head to
 //            claim, [16 + q] unit ticket of XCD queue q
-//   heads    int32[kMaxQueues * BH]: head claimed by each local head slot of a queue
-//   counters int32[BH * n_qsub]: per (head, query sub-tile) dQ turn counter
+//   heads    int32[kMaxQueues][heads_row]: head claimed by each local head slot
+//            of a queue (rows padded to 256 bytes: one queue per cache line set)
+//   flags    int32[BH][flag_stride]: per (head, query sub-tile, dQ wave) the
+//            number of contributions that wave has handed over (rows padded to
+//            256 bytes, so no two heads share a cache line)
 //   lse2     fp32[BH * S_pad]: lse * log2(e), +inf on padding rows
 //   delta    fp32[BH * S_pad]: rowsum(dO * O), 0 on padding rows
 //   dq_ws    fp32[BH * S_pad * D]: dQ accumulator
 //   park     fp32[kMaxGrid * 2 * T * D * 2]: Symmetric Shift only; per workgroup,
 //            one slot per KV tile of its pair, each holding dK and dV
 struct WsLayout {
-  size_t header, heads, counters, lse2, delta, dq_ws, park, total;
+  size_t header, heads, flags, lse2, delta, dq_ws, park, total;
+  long long heads_row, flag_stride;  // int32 elements per queue row / per head
 };
+
+// dQ waves per workgroup for a KV tile edge T (one per 32 keys)
+inline int dq_waves(int T) { return T / 32; }
+
+inline long long align64(long long x) { return (x + 63) & ~63ll; }
 
 inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, bool park) {
   WsLayout w;
+  w.heads_row = align64(BH);
+  w.flag_stride = align64((long long)n_qsub * dq_waves(T));
   size_t off = 0;
   w.header = off;   off += align256(64 * sizeof(int));
-  w.heads = off;    off += align256(size_t(kMaxQueues) * BH * sizeof(int));
-  w.counters = off; off += align256(size_t(BH) * n_qsub * sizeof(int));
+  w.heads = off;    off += align256(size_t(kMaxQueues) * w.heads_row * sizeof(int));
+  w.flags = off;    off += align256(size_t(BH) * w.flag_stride * sizeof(int));
   w.lse2 = off;     off += align256(size_t(BH) * S_pad * sizeof(float));
   w.delta = off;    off += align256(size_t(BH) * S_pad * sizeof(float));
   w.dq_ws = off;    off += align256(size_t(BH) * S_pad * D * sizeof(float));

@@ -86,7 +86,7 @@ int attn_bwd_tile(int S, int D, int tile_request);
 /*
  * attn_bwd_workspace_size - bytes of device workspace a backward call needs.
  * The workspace holds the fp32 dQ accumulator (B*H*ceil(S/T)*T*D floats), the
- * per-row softmax terms, the dQ ordering counters and, for Symmetric Shift,
+ * per-row softmax terms, the dQ hand-off flags and, for Symmetric Shift,
  * the parking area for a worker's second set of dK/dV accumulators.
  * Returns 0 for invalid arguments (then the call itself reports why).
  */
@@ -98,8 +98,9 @@ size_t attn_bwd_workspace_size(int B, int H, int S, int D, int mask, int schedul
  *   Out: dq, dk, dv (bf16 [B][H][S][D]); overwritten, no accumulation.
  *   Each workgroup owns one KV tile (two for Symmetric Shift) and keeps its
  *   dK/dV in registers; dQ tile i is accumulated in fp32 in the order the
- *   schedule fixes, each contributor waiting for its turn on a per-tile
- *   counter. The dQ accumulation uses no floating-point atomics.
+ *   schedule fixes, each contributor waiting for its turn on per-sub-tile
+ *   hand-off flags: the order of the fp32 additions into every dQ element is
+ *   the schedule's, never the hardware's.
  *   schedule: attn_schedule_t. NAIVE, DESCENDING and SHIFT take either
  *   mask (SHIFT on a causal mask: worker j walks query tiles j..N-1, dQ tile i
  *   accumulates KV tiles i, i-1, ..., 0); SYMMETRIC_SHIFT needs
@@ -150,13 +151,13 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
 
 /*
  * attn_debug_set_wait_limit - bound (in polling iterations, each one a
- * counter load plus a short sleep) on a single dQ ordering wait; 0 restores
- * the default (about 2^24). When a wait reaches the bound the workgroup
- * records ATTN_ERR_TIMEOUT in the workspace, stops waiting and finishes
- * normally; attn_bwd_check reports it. poison_counter != 0 makes the next
- * deterministic calls start one dQ counter at an unreachable value so that the
- * bound is certain to trip (used to test the timeout path). Process-wide,
- * not thread-safe; for tests only.
+ * hand-off flag read plus a short sleep) on a single dQ ordering wait; 0
+ * restores the default (2^21, a few seconds at most). When a wait reaches the bound the
+ * workgroup records ATTN_ERR_TIMEOUT in the workspace, stops waiting and
+ * finishes normally; attn_bwd_check reports it. poison_counter != 0 makes the
+ * next deterministic calls wait on one dQ hand-off flag for a value it never
+ * takes, so that the bound is certain to trip (used to test the timeout
+ * path). Process-wide, not thread-safe; for tests only.
  */
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
 
@@ -176,7 +177,8 @@ int attn_debug_wait_timeouts(int reset);
  *   0 (default) choose per call: XCD-local when every worker of a head can be
  *     resident on one XCD (always for NAIVE/DESCENDING; for SHIFT and
  *     SYMMETRIC_SHIFT when the workers per head fit the XCD), else 1;
- *   1 device-scope atomic read-modify-writes, serialised by the counters;
+ *   1 device-scope atomic read-modify-writes, serialised by the hand-off
+ *     flags (themselves atomics);
  *   2 XCD-local: all workers of a head run on one XCD and update the fp32
  *     accumulator with plain loads/stores through that XCD's L2 (falls back
  *     to 1 where the workers of a head would not be co-resident).
