@@ -507,6 +507,16 @@ struct DqRole {
     return t.q * G::T + (i % NSUB) * BR;
   }
 
+  // Staging piece gi: rows 4 qg .. 4 qg + 3, features 8 dg .. 8 dg + 7. Each run
+  // of 16 lanes covers 16 different qg (so the transposed writes of a run fill
+  // 16 different bank pairs), and the feature chunk is rotated by qg / 2 so
+  // that the 8 lanes of each 16-byte row-major write land on 8 different bank
+  // quads (rows 4 qg + rr alone would repeat every second lane).
+  __device__ __forceinline__ static void piece(int gi, int& qg, int& dg) {
+    qg = gi % (BR / 4);
+    dg = (gi / (BR / 4) + (qg >> 1)) % (D / 8);
+  }
+
   // Rows past the end of the sequence are read as copies of the last row: the
   // masks give them P = 0 exactly, so a finite duplicate contributes nothing.
   __device__ __forceinline__ void stage_load(int bh, int qrow0) {
@@ -516,7 +526,8 @@ struct DqRole {
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tb + g * G::NTB;
-      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
+      int qg, dg;
+      piece(gi, qg, dg);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int row = min(qrow0 + qg * 4 + rr, S - 1);
@@ -537,7 +548,8 @@ struct DqRole {
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tb + g * G::NTB;
-      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
+      int qg, dg;
+      piece(gi, qg, dg);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         *(u32x4*)&Q[(qg * 4 + rr) * G::DP + dg * 8] = stq[g][rr];
@@ -556,7 +568,8 @@ struct DqRole {
 #pragma unroll
     for (int g = 0; g < GPT; ++g) {
       const int gi = tb + g * G::NTB;
-      const int qg = gi % (BR / 4), dg = gi / (BR / 4);
+      int qg, dg;
+      piece(gi, qg, dg);
       const int pos = quad_pos(qg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -656,13 +669,18 @@ struct DqRole {
   __device__ __forceinline__ unsigned elem_off(int j, int e) const { return blk_base(j) + 4u * (64 * e + lane); }
   __device__ __forceinline__ unsigned quad_off(int j, int g) const { return blk_base(j) + 16u * (64 * g + lane); }
 
-  __device__ __forceinline__ void acquire(const Seg& sg, int j) {
+  // dQ partial of sub-tile j from the dS rows in registers
+  __device__ __forceinline__ void dq_mma() {
 #pragma unroll
     for (int x = 0; x < QBW; ++x) {
       acc[x] = zero16();
 #pragma unroll
       for (int c = 0; c < TC; ++c) acc[x] = mfma32(dsA[c], Kd[x][c], acc[x]);
     }
+  }
+
+  // where sub-tile j's partial goes; wait for its turn; start the running-sum loads
+  __device__ __forceinline__ void acquire(const Seg& sg, int j) {
     const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + j / NSUB);
     // this wave's flag for the sub-tile: dQ wave b of every contributor updates
     // the same blocks of the accumulator, so it waits only for wave b of the
@@ -740,32 +758,48 @@ struct DqRole {
         }
       }
     }
+    asm volatile("" ::: "memory");
     if (!h_last) {
       pend = h_flag;
       pend_val = h_r + 1;
     }
   }
 
+  // The hand-off of sub-tile j is spread over two intervals so that the
+  // tile waves never wait at barrier X for dQ work and every memory latency
+  // has time to pass:
+  //   interval j+1, before X: dS of j to registers (the tile waves overwrite
+  //            dS^T after X); after X: dQ = dS K, wait for the turn, start the
+  //            running-sum loads;
+  //   interval j+2, after X:  add and store; hand over once the stores have
+  //            completed, which the dQ MFMAs of j+1 leave time for.
+  // Before X a dQ wave only moves LDS data (dS of the previous sub-tile out,
+  // the transposed Q/dO of this one in) and starts the next staging loads.
+  // A wave hands sub-tile j over before it waits for its turn on j+1, so each
+  // wait depends only on hand-overs that no later wait of their wave precedes:
+  // with cyclic schedules (Shift, Symmetric Shift) this is what keeps the waits
+  // free of cycles.
   __device__ __forceinline__ void part1(const Seg& sg, int i) {
     if (i > 0) {
-      // (order matters for the memory counters: the staged registers are
-      // consumed before the running-sum loads are issued, and those before the
-      // next staging loads, so no step waits for a younger load)
       read_ds();
-      release();  // wait for the previous sub-tile's stores, before any new load is issued
       write_tr();
-      acquire(sg, i - 1);
       if (i + 1 < sg.n) stage_load(sg.bh, sub_row0(sg, i + 1));
     }
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
-    if (i > 0) commit();
+    // (the running sums of i-2 were loaded an interval ago)
+    if (i > 1) commit();              // sub-tile i-2
+    if (i > 0) dq_mma();              // sub-tile i-1
+    release();                        // sub-tile i-2
+    if (i > 0) acquire(sg, i - 1);    // sub-tile i-1
     if (i + 1 < sg.n) write_rm((i + 1) & 1);
   }
 
   __device__ __forceinline__ void seg_end(const Seg& sg) {
-    read_ds();
+    read_ds();                        // dS of the last sub-tile
+    if (sg.n > 1) commit();           // sub-tile n-2
+    dq_mma();                         // sub-tile n-1
     release();
     acquire(sg, sg.n - 1);
     commit();
