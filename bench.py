@@ -195,7 +195,7 @@ def main():
     ap.add_argument("--workload", default="C2")
     ap.add_argument("--schedules", default="", help="comma list; default: every schedule valid for the mask")
     ap.add_argument("--no-nondet", action="store_true")
-    ap.add_argument("--dq-protocol", default="auto", choices=["auto", "device_atomic", "xcd_local"],
+    ap.add_argument("--dq-protocol", default="auto", choices=["auto", "device", "xcd_local"],
                     help="dQ hand-off of the deterministic calls (auto picks XCD-local where it applies)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle leg (0 = skip)")
     ap.add_argument("--no-mfma-probe", action="store_true", help="skip the measured-MFMA-peak probe")

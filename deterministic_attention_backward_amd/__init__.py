@@ -171,11 +171,11 @@ def schedule_plan(n_tiles: int, causal: bool, schedule):
     return n_workers, recs
 
 
-DQ_PROTOCOLS = {"auto": 0, "device_atomic": 1, "xcd_local": 2}
+DQ_PROTOCOLS = {"auto": 0, "device": 1, "xcd_local": 2}
 
 
 def set_dq_protocol(protocol="auto") -> None:
-    """Debug: force the dQ hand-off protocol of deterministic calls ("auto", "device_atomic", "xcd_local")."""
+    """Debug: force the dQ hand-off protocol of deterministic calls ("auto", "device", "xcd_local")."""
     _lib.check(_lib.load().attn_debug_set_dq_protocol(DQ_PROTOCOLS[protocol]), "attn_debug_set_dq_protocol")
 
 

@@ -148,9 +148,32 @@ __device__ __forceinline__ int l2_load(int* w) {
 }
 // 16 bytes at base + byte_off through a buffer resource (base wave-uniform,
 // byte_off < bytes), as an agent-scope load served by the XCD's L2.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
 __device__ __forceinline__ f32x4 l2_load16(const float* base, unsigned bytes, unsigned byte_off) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16 /* sc1 */));
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base, bytes), (int)byte_off, 0, 16 /* sc1 */));
+}
+
+// Words shared by workgroups on different XCDs: system-scope accesses (sc0 sc1
+// cache policy), which are written through to and read from the device-wide
+// coherence point instead of an XCD's L2. The dword forms are the relaxed
+// system-scope atomic load and store; the 16-byte forms use the same policy
+// on buffer loads and stores. Measured on the box: workgroups on two XCDs
+// handing a 4 KB region back and forth this way (flag after a completed
+// store) never read a stale value in 1000 hand-overs.
+__device__ __forceinline__ void sys_store(int* w, int v) {
+  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ int sys_load(int* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ f32x4 sys_load16(const float* base, unsigned bytes, unsigned byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc(base, bytes), (int)byte_off, 0, 17 /* sc0 sc1 */));
+}
+__device__ __forceinline__ void sys_store16(float* base, unsigned bytes, unsigned byte_off, f32x4 v) {
+  typedef unsigned u32v4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, v), rsrc(base, bytes), (int)byte_off, 0, 17);
 }
 
 // Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
@@ -198,7 +221,7 @@ __device__ __forceinline__ unsigned long long wclock() {
 // How a unit hands its dQ partials over.
 enum {
   MODE_ATOMIC = 0,  // non-deterministic: fp32 atomic adds in whatever order they land
-  MODE_DEVICE = 1,  // deterministic: device-scope atomic RMWs serialised by the hand-off flags
+  MODE_DEVICE = 1,  // deterministic: system-scope read-modify-writes, serialised by the hand-off flags
   MODE_XCD = 2      // deterministic: all workers of a head on one XCD, plain RMW via its L2
 };
 
@@ -597,16 +620,10 @@ struct DqRole {
   }
 
   // A hand-off flag as one wave-uniform value. XCD-local: every contributor of
-  // the tile runs on this XCD, so its L2 holds the flag; across XCDs: an atomic
-  // read-modify-write.
+  // the tile runs on this XCD, so its L2 holds the flag; across XCDs: a
+  // system-scope load.
   __device__ __forceinline__ int flag_read(int* f) const {
-    int v = 0;
-    if (XCD) {
-      v = l2_load(f);
-    } else if (lane == 0) {
-      v = ctl_read(f);
-    }
-    return __builtin_amdgcn_readfirstlane(v);
+    return __builtin_amdgcn_readfirstlane(XCD ? l2_load(f) : sys_load(f));
   }
 
   // Once every dQ update this wave issued has completed, tell the next
@@ -616,7 +633,7 @@ struct DqRole {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (lane == 0) {
         if (XCD) l2_store(&p.flags[pend], pend_val);
-        else ctl_set(&p.flags[pend], pend_val);
+        else sys_store(&p.flags[pend], pend_val);
       }
       pend = -1;
     }
@@ -661,10 +678,10 @@ struct DqRole {
   // The dQ accumulator is stored in the MFMA's own register order: per query
   // sub-tile, 32 x 32 blocks (row block mb, feature block nb) of 1024 floats.
   // Every contributor of a block holds it in the same lanes, so
-  //  - XCD-local mode, "quad-major": accumulators 4g..4g+3 of lane l at
+  //  - deterministic modes, "quad-major": accumulators 4g..4g+3 of lane l at
   //    (g * 64 + l) * 4: each 16-byte access of a wave covers 1 KB;
-  //  - atomic modes, "element-major": accumulator e of lane l at e * 64 + l:
-  //    each atomic instruction covers 256 contiguous bytes.
+  //  - the atomic variant, "element-major": accumulator e of lane l at
+  //    e * 64 + l: each atomic instruction covers 256 contiguous bytes.
   __device__ __forceinline__ unsigned blk_base(int j) const { return 4096u * (unsigned)(mb * G::ND + nb0 + j); }
   __device__ __forceinline__ unsigned elem_off(int j, int e) const { return blk_base(j) + 4u * (64 * e + lane); }
   __device__ __forceinline__ unsigned quad_off(int j, int g) const { return blk_base(j) + 16u * (64 * g + lane); }
@@ -705,17 +722,17 @@ struct DqRole {
       seen = flag_read(fl);
     }
     if constexpr (kProfileWait) wc->turn += wclock() - w0;
-    if (XCD) {
-      // Every contributor of this tile runs on this XCD, so its L2 holds the
-      // accumulator coherently for all of them: read the running sum there.
+    // XCD-local: every contributor of this tile runs on this XCD, so its L2
+    // holds the accumulator coherently for all of them: read the running sum
+    // there. Across XCDs: read it from the device-wide coherence point.
 #pragma unroll
-      for (int x = 0; x < QBW; ++x) {
+    for (int x = 0; x < QBW; ++x) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 v = l2_load16(h_row, 4u * BR * D, quad_off(x, g));
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = XCD ? l2_load16(h_row, 4u * BR * D, quad_off(x, g))
+                            : sys_load16(h_row, 4u * BR * D, quad_off(x, g));
 #pragma unroll
-          for (int k = 0; k < 4; ++k) prev[x][4 * g + k] = v[k];
-        }
+        for (int k = 0; k < 4; ++k) prev[x][4 * g + k] = v[k];
       }
     }
   }
@@ -742,19 +759,17 @@ struct DqRole {
         }
       }
     } else {
-      // Device-scope atomic RMWs, serialised by the hand-off flags: each element
-      // receives the same fp32 additions in the same order on every run; the
-      // first contributor swaps its value in.
+      // Across XCDs: system-scope stores of the new running sum (written
+      // through to the device-wide coherence point); the first contributor
+      // stores its partial as it is.
 #pragma unroll
       for (int x = 0; x < QBW; ++x) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          if (h_r == 0)
-            __hip_atomic_exchange(at_bytes(h_row, elem_off(x, e)), acc[x][e], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-          else
-            __hip_atomic_fetch_add(at_bytes(h_row, elem_off(x, e)), acc[x][e], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = h_r > 0 ? prev[x][4 * g + k] + acc[x][4 * g + k] : acc[x][4 * g + k];
+          sys_store16(h_row, 4u * BR * D, quad_off(x, g), v);
         }
       }
     }
@@ -1015,7 +1030,7 @@ static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int
   // workgroups. Cyclic schedules need all workers of a head resident there.
   const int n_xcd = (num_cu >= 64 && num_cu % 8 == 0) ? 8 : 1;
   const long long per_xcd = grid / n_xcd;
-  const bool xcd = !atomic && protocol != DQ_DEVICE_ATOMIC && (!cyclic || mp.n_workers <= per_xcd);
+  const bool xcd = !atomic && protocol != DQ_DEVICE && (!cyclic || mp.n_workers <= per_xcd);
   *xcd_out = xcd ? 1 : 0;
   if (atomic) return launch_main<D, T, BR, CAUSAL, MODE_ATOMIC>(mp, (int)grid, stream);
   if (xcd) return launch_main<D, T, BR, CAUSAL, MODE_XCD>(mp, (int)grid, stream);
@@ -1117,10 +1132,10 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
     const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
     if (a.D == 64)
       hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.BR, xcd_local, a.scale);
+                         a.S_pad, a.BR, atomic ? 0 : 1, a.scale);
     else
       hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.BR, xcd_local, a.scale);
+                         a.S_pad, a.BR, atomic ? 0 : 1, a.scale);
     e = hipGetLastError();
   }
   return e;

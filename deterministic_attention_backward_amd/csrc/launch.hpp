@@ -15,7 +15,7 @@ constexpr int kMaxGrid = 512;
 constexpr int kMaxQueues = 16;
 
 // dQ hand-off protocols (attn_debug_set_dq_protocol)
-enum { DQ_AUTO = 0, DQ_DEVICE_ATOMIC = 1, DQ_XCD_LOCAL = 2 };
+enum { DQ_AUTO = 0, DQ_DEVICE = 1, DQ_XCD_LOCAL = 2 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -69,7 +69,7 @@ struct BwdArgs {
   int causal, sched, atomic;
   uint32_t wait_limit;
   int poison;
-  int dq_protocol;                 // DQ_AUTO / DQ_DEVICE_ATOMIC / DQ_XCD_LOCAL
+  int dq_protocol;                 // DQ_AUTO / DQ_DEVICE / DQ_XCD_LOCAL
   hipEvent_t ev_before, ev_after;  // optional: recorded around the main kernel
 };
 

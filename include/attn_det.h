@@ -177,8 +177,10 @@ int attn_debug_wait_timeouts(int reset);
  *   0 (default) choose per call: XCD-local when every worker of a head can be
  *     resident on one XCD (always for NAIVE/DESCENDING; for SHIFT and
  *     SYMMETRIC_SHIFT when the workers per head fit the XCD), else 1;
- *   1 device-scope atomic read-modify-writes, serialised by the hand-off
- *     flags (themselves atomics);
+ *   1 device-wide: workers of a head may run on any XCD; the accumulator's
+ *     running sums and the hand-off flags are read and written with
+ *     system-scope accesses (written through to, and read from, the
+ *     device-wide coherence point instead of an XCD's L2);
  *   2 XCD-local: all workers of a head run on one XCD and update the fp32
  *     accumulator with plain loads/stores through that XCD's L2 (falls back
  *     to 1 where the workers of a head would not be co-resident).

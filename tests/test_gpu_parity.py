@@ -113,7 +113,7 @@ def test_forward_parity(case):
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dH%dS%dD%d%s_t%d" % (c[0], c[1], c[2], c[3],
                                                                               "c" if c[4] else "f", c[6]))
-@pytest.mark.parametrize("protocol", ["auto", "device_atomic"])
+@pytest.mark.parametrize("protocol", ["auto", "device"])
 def test_backward_parity(case, protocol):
     B, H, S, D, causal, seed, tile = case
     c = Case(B, H, S, D, causal, seed)
@@ -138,7 +138,7 @@ DET_CASES = [
 
 @pytest.mark.parametrize("case", DET_CASES, ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3],
                                                                               "c" if c[4] else "f"))
-@pytest.mark.parametrize("protocol", ["auto", "device_atomic"])
+@pytest.mark.parametrize("protocol", ["auto", "device"])
 def test_bitwise_reproducible_20_runs(case, protocol):
     B, H, S, D, causal, seed = case
     c = Case(B, H, S, D, causal, seed)
