@@ -1011,8 +1011,7 @@ static hipError_t launch_main(const MainParams& mp, int grid, hipStream_t stream
 }
 
 template <int D, int T, int BR, bool CAUSAL>
-static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int protocol, hipStream_t stream,
-                              int* xcd_out) {
+static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int protocol, hipStream_t stream) {
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &per_cu, bwd_main_kernel<D, T, BR, CAUSAL, MODE_DEVICE>, T / 16 * 64, 0);
@@ -1031,7 +1030,6 @@ static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int
   const int n_xcd = (num_cu >= 64 && num_cu % 8 == 0) ? 8 : 1;
   const long long per_xcd = grid / n_xcd;
   const bool xcd = !atomic && protocol != DQ_DEVICE && (!cyclic || mp.n_workers <= per_xcd);
-  *xcd_out = xcd ? 1 : 0;
   if (atomic) return launch_main<D, T, BR, CAUSAL, MODE_ATOMIC>(mp, (int)grid, stream);
   if (xcd) return launch_main<D, T, BR, CAUSAL, MODE_XCD>(mp, (int)grid, stream);
   return launch_main<D, T, BR, CAUSAL, MODE_DEVICE>(mp, (int)grid, stream);
@@ -1039,9 +1037,9 @@ static hipError_t launch_mask(const MainParams& mp, bool atomic, int num_cu, int
 
 template <int D, int T, int BR>
 static hipError_t dispatch_mask(const MainParams& mp, bool causal, bool atomic, int num_cu, int protocol,
-                                hipStream_t s, int* xcd) {
-  return causal ? launch_mask<D, T, BR, true>(mp, atomic, num_cu, protocol, s, xcd)
-                : launch_mask<D, T, BR, false>(mp, atomic, num_cu, protocol, s, xcd);
+                                hipStream_t s) {
+  return causal ? launch_mask<D, T, BR, true>(mp, atomic, num_cu, protocol, s)
+                : launch_mask<D, T, BR, false>(mp, atomic, num_cu, protocol, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
@@ -1110,17 +1108,16 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.scale_log2 = a.scale * 1.4426950408889634f;
   mp.wait_limit = a.wait_limit;
 
-  int xcd_local = 0;
   hipError_t e = hipErrorInvalidValue;
   const bool causal = a.causal != 0, atomic = a.atomic != 0;
   if (a.ev_before && a.ev_after) {
     e = hipEventRecord(a.ev_before, stream);
     if (e != hipSuccess) return e;
   }
-  if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
-  else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
-  else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
-  else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream, &xcd_local);
+  if (a.D == 128 && a.T == 128) e = dispatch_mask<128, 128, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream);
+  else if (a.D == 128 && a.T == 64) e = dispatch_mask<128, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream);
+  else if (a.D == 64 && a.T == 128) e = dispatch_mask<64, 128, 128>(mp, causal, atomic, num_cu, a.dq_protocol, stream);
+  else if (a.D == 64 && a.T == 64) e = dispatch_mask<64, 64, 64>(mp, causal, atomic, num_cu, a.dq_protocol, stream);
   if (e != hipSuccess) return e;
   if (a.ev_before && a.ev_after) {
     e = hipEventRecord(a.ev_after, stream);
