@@ -106,16 +106,18 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
 //     keys' K and V rows (B operands of S = Q K^T and dP = dO V^T) and their dK
 //     and dV accumulators for the whole run of tasks on the tile. Per query
 //     sub-tile of BR rows it computes S, dP, P and dS, writes dS^T to LDS and
-//     accumulates dV += P^T dO and dK += dS^T Q.
+//     accumulates dV += P^T dO and dK += dS^T Q, reading the staged Q and dO
+//     rows both row-wise (A operands) and transposed (B operands, through the
+//     transposing LDS read).
 //   dQ waves (T/32): stage the query sub-tiles (Q, dO, LSE, Delta) from HBM into
-//     LDS and, one sub-tile behind the tile waves, compute dQ = dS K from the
-//     dS^T the tile waves left in LDS (K columns held in registers) and hand the
-//     partial over to the fp32 dQ workspace in the schedule's order.
+//     LDS with DMA loads (no registers involved) and, one sub-tile behind the
+//     tile waves, compute dQ = dS K from the dS^T the tile waves left in LDS
+//     (K columns held in registers) and hand the partial over to the fp32 dQ
+//     workspace in the schedule's order.
 // Two workgroup barriers per sub-tile order the hand-over between the roles
-// (X: the dQ waves are done with the previous dS^T and have written this
-// sub-tile's transposed Q/dO; Y: the tile waves are done with the sub-tile).
-// Row-major Q/dO are double-buffered; the transposed copies and dS^T are
-// single-buffered and protected by those two barriers.
+// (X: the dQ waves are done with the previous dS^T; Y: the tile waves are done
+// with the sub-tile and the next one has landed). The staged rows are
+// double-buffered; dS^T is single-buffered and protected by the two barriers.
 
 struct MainParams {
   const bf16 *q, *k, *v;
@@ -186,8 +188,21 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// quads of each 16-query group in transposed LDS rows are stored in the order 0, 2, 1, 3
-__device__ __forceinline__ int quad_pos(int qg) { return 16 * (qg >> 2) + 4 * ((qg & 1) * 2 + ((qg >> 1) & 1)); }
+// Staged query rows (Q, dO) hold D bf16 without padding, in 16-byte chunks;
+// chunk c of row r sits at position c ^ swz(r). With 64 LDS banks of 4 bytes,
+// a 16-byte read serves 16 lanes per pass and an 8-byte read 32 lanes:
+//  - row-wise reads (16 consecutive rows, one chunk each) land on 16
+//    different positions (D = 128: 256-byte rows, swz bijective on r mod 16;
+//    D = 64: 128-byte rows, swz bijective on the even and on the odd rows);
+//  - transposed reads (4 consecutive rows, 4 consecutive chunks of an aligned
+//    group) land on 16 different positions, because swz gives 4 consecutive
+//    rows (D = 64: the two of each parity) different bits above the two lowest.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dims");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // Workgroup barrier over LDS only: this wave's LDS operations complete
 // (lgkmcnt(0)) before it arrives; its global loads and stores stay in flight.
@@ -231,9 +246,8 @@ struct Geo {
   static constexpr int NA = T / 32;            // tile waves
   static constexpr int NB = NA;                // dQ waves
   static constexpr int NTA = NA * 64, NTB = NB * 64, NT = NTA + NTB;
-  static constexpr int DP = D + 8;             // row-major Q/dO rows (bf16 elements)
-  static constexpr int BRP = BR + 8;           // transposed Q/dO rows
-  static constexpr int TP = T + 8;             // transposed K rows
+  static constexpr int DP = D + 8;             // padded K and V rows (bf16 elements)
+  static constexpr int RB = 2 * D;             // staged Q/dO row (bytes, swizzled chunks)
   static constexpr int SP = BR + 4;            // transposed dS rows
   static constexpr int KC = D / 16;            // k-chunks over the features
   static constexpr int ND = D / 32;            // 32-wide feature blocks
@@ -241,13 +255,14 @@ struct Geo {
   static constexpr int NSUB = T / BR;          // sub-tiles per task
   static constexpr int TC = T / 16;            // k-chunks over the keys
   static constexpr int QBW = MB * ND / NB;     // dQ blocks per dQ wave: one row block, QBW feature blocks
-  static constexpr int GROUPS = (BR / 4) * (D / 8);  // staging pieces: 4 rows x 8 features
-  static constexpr int GPT = GROUPS / NTB;
+  // staging: LDS DMA pieces of 1 KB (64 lanes x 16 bytes), Q then dO
+  static constexpr int PIECES = 2 * BR * RB / 1024;
+  static constexpr int PPW = PIECES / NA;      // per tile wave
   // LDS regions (bytes)
-  static constexpr int RM_BYTES = 2 * BR * DP * 2 + 2 * BR * 4;  // one row-major buffer: Q, dO, LSE, Delta
-  static constexpr int TR_OFF = 2 * RM_BYTES;
-  static constexpr int TR_BYTES = 2 * D * BRP * 2;               // Q^T, dO^T (K^T at a tile start)
-  static constexpr int DS_OFF = TR_OFF + TR_BYTES;
+  static constexpr int RM_BYTES = 2 * BR * RB + 2 * BR * 4;  // one staging buffer: Q, dO, LSE, Delta
+  static constexpr int KT_OFF = 2 * RM_BYTES;
+  static constexpr int KT_BYTES = T * DP * 2;                // K rows, read transposed by the dQ waves
+  static constexpr int DS_OFF = KT_OFF + KT_BYTES;
   static constexpr int DS_BYTES = T * SP * 2;
   // D = 128: the tile waves keep V in LDS (row-major, each wave reads only the
   // rows it wrote) so that K, dK and dV fit their registers without spilling
@@ -257,21 +272,18 @@ struct Geo {
   static constexpr int UNIT_OFF = SV_OFF + SV_BYTES;
   static constexpr int LDS_BYTES = UNIT_OFF + 16;
   static_assert(QBW >= 1 && QBW * NB == MB * ND && QBW <= ND && ND % QBW == 0, "dQ block split");
-  static_assert(GPT >= 1 && GROUPS % NTB == 0 && T % BR == 0 && BR <= NTB, "staging split");
-  static_assert(T * DP * 2 <= TR_BYTES, "the K rows must fit the transposed staging area");
+  static_assert(PPW >= 1 && PIECES % NA == 0 && T % BR == 0 && BR % 64 == 0 && NA >= 2, "staging split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 template <class G>
 struct Lds {
   char* base;
-  __device__ __forceinline__ bf16* q(int b) const { return (bf16*)(base + b * G::RM_BYTES); }
-  __device__ __forceinline__ bf16* o(int b) const { return q(b) + G::BR * G::DP; }
-  __device__ __forceinline__ float* lse(int b) const { return (float*)(base + b * G::RM_BYTES + 2 * G::BR * G::DP * 2); }
+  __device__ __forceinline__ char* q(int b) const { return base + b * G::RM_BYTES; }
+  __device__ __forceinline__ char* o(int b) const { return q(b) + G::BR * G::RB; }
+  __device__ __forceinline__ float* lse(int b) const { return (float*)(base + b * G::RM_BYTES + 2 * G::BR * G::RB); }
   __device__ __forceinline__ float* dl(int b) const { return lse(b) + G::BR; }
-  __device__ __forceinline__ bf16* qt() const { return (bf16*)(base + G::TR_OFF); }
-  __device__ __forceinline__ bf16* ot() const { return qt() + G::D * G::BRP; }
-  __device__ __forceinline__ bf16* kt() const { return qt(); }
+  __device__ __forceinline__ bf16* kt() const { return (bf16*)(base + G::KT_OFF); }
   __device__ __forceinline__ bf16* dst() const { return (bf16*)(base + G::DS_OFF); }
   __device__ __forceinline__ bf16* v() const { return (bf16*)(base + G::SV_OFF); }
   __device__ __forceinline__ int* unit() const { return (int*)(base + G::UNIT_OFF); }
@@ -293,6 +305,10 @@ struct TileRole {
   const MainParams& p;
   Lds<G> L;
   int tid, lane, a, l32, hh;
+  // staged-row addressing (see swz): row-wise reads of row l32, chunk 2c + hh at
+  // a_base + 32 (c ^ sw1); transposed reads, 4 rows from 4 hh + e, features
+  // from 32 n + 16 (group & 1) + 4 t, at tr_base[part] + 64 (n ^ thi)
+  int a_base, sw1, tr_base[2], thi;
   static constexpr bool VL = G::V_LDS;
   bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
@@ -302,9 +318,17 @@ struct TileRole {
   __device__ __forceinline__ TileRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
     tid = threadIdx.x;
     lane = tid & 63;
-    a = tid >> 6;
+    a = __builtin_amdgcn_readfirstlane(tid >> 6);
     l32 = lane & 31;
     hh = lane >> 5;
+    const int sw = swz<G::D>(l32);
+    a_base = l32 * G::RB + 16 * ((hh ^ sw) & 1);
+    sw1 = sw >> 1;
+    const int g = lane >> 4, e = (lane >> 2) & 3, t = lane & 3;
+    thi = G::D == 128 ? e : e >> 1;
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+      tr_base[part] = (4 * hh + e) * G::RB + 16 * ((2 * (g & 1) + (t >> 1)) ^ (2 * part + hh)) + 8 * (t & 1);
   }
 
   __device__ __forceinline__ void park(const Seg& sg, bool load) {
@@ -358,22 +382,27 @@ struct TileRole {
 
   // S and dP of row block m, turned into P and dS in place
   __device__ __forceinline__ void sdp(int m, int buf, int q_base, int kv_base, bool need_mask) {
-    const bf16* Q = &L.q(buf)[(32 * m + l32) * G::DP + 8 * hh];
-    const bf16* O = &L.o(buf)[(32 * m + l32) * G::DP + 8 * hh];
+    // (the lane constants are re-read here so that the compiler computes the
+    // swizzled addresses where they are used instead of keeping them all live)
+    int ab = a_base, s1 = sw1;
+    asm volatile("" : "+v"(ab), "+v"(s1));
+    const char* Q = L.q(buf) + 32 * m * G::RB + ab;
+    const char* O = L.o(buf) + 32 * m * G::RB + ab;
     const bf16* V = &L.v()[(32 * a + l32) * G::DP + 8 * hh];
     s = zero16();
     dp = zero16();
     // operands one k-chunk ahead; the scheduling fences keep at most two
     // chunks of operands live (the resident K/dK/dV leave little room)
     bf16x8 qa[2], oa[2], vb[2];
-    qa[0] = *(const bf16x8*)&Q[0];
-    oa[0] = *(const bf16x8*)&O[0];
+    qa[0] = *(const bf16x8*)(Q + (s1 << 5));
+    oa[0] = *(const bf16x8*)(O + (s1 << 5));
     if constexpr (VL) vb[0] = *(const bf16x8*)&V[0];
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       if (c + 1 < KC) {
-        qa[(c + 1) & 1] = *(const bf16x8*)&Q[16 * (c + 1)];
-        oa[(c + 1) & 1] = *(const bf16x8*)&O[16 * (c + 1)];
+        const int co = ((c + 1) ^ s1) << 5;
+        qa[(c + 1) & 1] = *(const bf16x8*)(Q + co);
+        oa[(c + 1) & 1] = *(const bf16x8*)(O + co);
         if constexpr (VL) vb[(c + 1) & 1] = *(const bf16x8*)&V[16 * (c + 1)];
       }
       s = mfma32(qa[c & 1], Kr[c], s);
@@ -417,7 +446,14 @@ struct TileRole {
   }
 
   // dS^T of row block m to LDS; dV += P^T dO and dK += dS^T Q
-  __device__ __forceinline__ void accumulate(int m) {
+  // B operand of feature block n, query half h2 of row block m: 8 queries in
+  // the order of the C-matrix rows the lane holds (4 hh + 0..3, 8 + 4 hh + 0..3)
+  __device__ __forceinline__ static bf16x8 trB(const char* blk, int h2, const int* tb, int nx) {
+    return cat44(lds_read_tr((const bf16*)(blk + 16 * h2 * G::RB + tb[0] + nx)),
+                 lds_read_tr((const bf16*)(blk + (16 * h2 + 8) * G::RB + tb[1] + nx)));
+  }
+
+  __device__ __forceinline__ void accumulate(int m, int buf) {
     const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
     const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
     bf16* drow = &L.dst()[(32 * a + l32) * G::SP + 32 * m + 4 * hh];  // four consecutive queries per write
@@ -425,21 +461,26 @@ struct TileRole {
     *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
     *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
     *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
-    const bf16* QT = &L.qt()[l32 * G::BRP + 32 * m + 8 * hh];
-    const bf16* OT = &L.ot()[l32 * G::BRP + 32 * m + 8 * hh];
+    int tb[2] = {tr_base[0], tr_base[1]}, th = thi;
+    asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
+    const char* QB = L.q(buf) + 32 * m * G::RB;
+    const char* OB = L.o(buf) + 32 * m * G::RB;
     bf16x8 ov[2][2], qv[2][2];  // B operands one feature block ahead
-    ov[0][0] = *(const bf16x8*)&OT[0];
-    ov[0][1] = *(const bf16x8*)&OT[16];
-    qv[0][0] = *(const bf16x8*)&QT[0];
-    qv[0][1] = *(const bf16x8*)&QT[16];
+    {
+      const int nx = th << 6;
+      ov[0][0] = trB(OB, 0, tb, nx);
+      ov[0][1] = trB(OB, 1, tb, nx);
+      qv[0][0] = trB(QB, 0, tb, nx);
+      qv[0][1] = trB(QB, 1, tb, nx);
+    }
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
       if (n + 1 < ND) {
-        const int ro = 32 * (n + 1) * G::BRP;
-        ov[(n + 1) & 1][0] = *(const bf16x8*)&OT[ro];
-        ov[(n + 1) & 1][1] = *(const bf16x8*)&OT[ro + 16];
-        qv[(n + 1) & 1][0] = *(const bf16x8*)&QT[ro];
-        qv[(n + 1) & 1][1] = *(const bf16x8*)&QT[ro + 16];
+        const int nx = ((n + 1) ^ th) << 6;
+        ov[(n + 1) & 1][0] = trB(OB, 0, tb, nx);
+        ov[(n + 1) & 1][1] = trB(OB, 1, tb, nx);
+        qv[(n + 1) & 1][0] = trB(QB, 0, tb, nx);
+        qv[(n + 1) & 1][1] = trB(QB, 1, tb, nx);
       }
       dVa[n] = mfma32(pb0, ov[n & 1][0], dVa[n]);
       dVa[n] = mfma32(pb1, ov[n & 1][1], dVa[n]);
@@ -467,11 +508,11 @@ struct TileRole {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    accumulate(0);
+    accumulate(0, i & 1);
 #pragma unroll
     for (int m = 1; m < MB; ++m) {
       sdp(m, i & 1, q_base, kv_base, need_mask);
-      accumulate(m);
+      accumulate(m, i & 1);
     }
   }
 
@@ -502,14 +543,12 @@ template <class G, bool CAUSAL, int MODE>
 struct DqRole {
   static constexpr bool ATOMIC = MODE == MODE_ATOMIC;
   static constexpr bool XCD = MODE == MODE_XCD;
-  static constexpr int QBW = G::QBW, TC = G::TC, GPT = G::GPT, NSUB = G::NSUB, BR = G::BR, D = G::D;
+  static constexpr int QBW = G::QBW, TC = G::TC, NSUB = G::NSUB, BR = G::BR, D = G::D;
   const MainParams& p;
   Lds<G> L;
   int tb, lane, b, l32, hh, mb, nb0;
   bf16x8 Kd[QBW][TC];   // B operand of dQ: this wave's feature columns, all keys of the tile
   bf16x8 dsA[TC];       // A operand of dQ: dS rows of this wave's row block
-  u32x4 stq[GPT][4], sto[GPT][4];  // staged query sub-tile
-  float stl = 0.0f, std_ = 0.0f;
   int pend = -1;      // flag this wave still owes a hand-over on
   int pend_val = 0;   // the value it will write there
   WaitClock* wc = nullptr;  // profiling build only
@@ -517,7 +556,7 @@ struct DqRole {
   __device__ __forceinline__ DqRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
     tb = threadIdx.x - G::NTA;
     lane = tb & 63;
-    b = tb >> 6;
+    b = __builtin_amdgcn_readfirstlane(tb >> 6);
     l32 = lane & 31;
     hh = lane >> 5;
     constexpr int per_row = G::ND / QBW;
@@ -525,89 +564,45 @@ struct DqRole {
     nb0 = QBW * (b % per_row);
   }
 
+  // LDS DMA of query rows q0 .. q0 + BR - 1 of head bh into staging buffer
+  // buf. Each instruction fills 1 KB of the buffer, lane L the 16 bytes at
+  // offset 16 L, so lane L fetches the chunk that the swizzle puts there. Rows
+  // past the end of the sequence are read as copies of the last row (the masks
+  // give them P = 0 exactly). LSE and Delta: one dword per lane.
+  __device__ __forceinline__ void stage(int bh, int q0, int buf) {
+    constexpr int CPR = G::D / 8, RPP = 64 / CPR, HALF = G::PIECES / 2;
+    const int S = p.S;
+    const bf16* qh = p.q + (size_t)bh * S * G::D;
+    const bf16* oh = p.dout + (size_t)bh * S * G::D;
+    // row r = RPP pr + rl: swz(r) = swz(RPP pr) ^ swz(rl) (disjoint bits)
+    int rl = lane / CPR, lx = (lane % CPR) ^ swz<G::D>(lane / CPR);
+    asm volatile("" : "+v"(rl), "+v"(lx));
+#pragma unroll
+    for (int k = 0; k < G::PPW; ++k) {
+      const int piece = b * G::PPW + k;  // wave-uniform
+      const bool is_o = piece >= HALF;
+      const int pr = is_o ? piece - HALF : piece;
+      const unsigned off =
+          (unsigned)(min(q0 + pr * RPP + rl, S - 1) * G::RB + 16 * (lx ^ swz<G::D>(pr * RPP)));
+      char* dst = (is_o ? L.o(buf) : L.q(buf)) + pr * 1024;
+      __builtin_amdgcn_global_load_lds(at_bytes(is_o ? oh : qh, off), (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                       0);
+    }
+    if (b < 2) {
+      const float* src = (b == 0 ? p.lse2 : p.delta) + (size_t)bh * p.S_pad;  // uniform
+      float* dst = b == 0 ? L.lse(buf) : L.dl(buf);
+#pragma unroll
+      for (int k = 0; k < G::BR / 64; ++k)
+        __builtin_amdgcn_global_load_lds(at_bytes(src, 4u * (unsigned)(q0 + 64 * k + lane)),
+                                         (__attribute__((address_space(3))) void*)(dst + 64 * k), 4, 0, 0);
+    }
+  }
+  // the DMA issued by this wave (and every older vector memory operation) has completed
+  __device__ __forceinline__ static void stage_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
   __device__ __forceinline__ int sub_row0(const Seg& sg, int i) const {
     const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.t0 + i / NSUB);
     return t.q * G::T + (i % NSUB) * BR;
-  }
-
-  // Staging piece gi: rows 4 qg .. 4 qg + 3, features 8 dg .. 8 dg + 7. Each run
-  // of 16 lanes covers 16 different qg (so the transposed writes of a run fill
-  // 16 different bank pairs), and the feature chunk is rotated by qg / 2 so
-  // that the 8 lanes of each 16-byte row-major write land on 8 different bank
-  // quads (rows 4 qg + rr alone would repeat every second lane).
-  __device__ __forceinline__ static void piece(int gi, int& qg, int& dg) {
-    qg = gi % (BR / 4);
-    dg = (gi / (BR / 4) + (qg >> 1)) % (D / 8);
-  }
-
-  // Rows past the end of the sequence are read as copies of the last row: the
-  // masks give them P = 0 exactly, so a finite duplicate contributes nothing.
-  __device__ __forceinline__ void stage_load(int bh, int qrow0) {
-    const int S = p.S;
-    const bf16* qh = p.q + (size_t)bh * S * D;  // uniform head bases
-    const bf16* oh = p.dout + (size_t)bh * S * D;
-#pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int gi = tb + g * G::NTB;
-      int qg, dg;
-      piece(gi, qg, dg);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = min(qrow0 + qg * 4 + rr, S - 1);
-        const unsigned off = 2u * (unsigned)(row * D + dg * 8);
-        stq[g][rr] = *at_bytes((const u32x4*)qh, off);
-        sto[g][rr] = *at_bytes((const u32x4*)oh, off);
-      }
-    }
-    if (tb < BR) {
-      stl = *at_bytes(p.lse2 + (size_t)bh * p.S_pad, 4u * (unsigned)(qrow0 + tb));
-      std_ = *at_bytes(p.delta + (size_t)bh * p.S_pad, 4u * (unsigned)(qrow0 + tb));
-    }
-  }
-
-  __device__ __forceinline__ void write_rm(int buf) {
-    bf16* Q = L.q(buf);
-    bf16* O = L.o(buf);
-#pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int gi = tb + g * G::NTB;
-      int qg, dg;
-      piece(gi, qg, dg);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        *(u32x4*)&Q[(qg * 4 + rr) * G::DP + dg * 8] = stq[g][rr];
-        *(u32x4*)&O[(qg * 4 + rr) * G::DP + dg * 8] = sto[g][rr];
-      }
-    }
-    if (tb < BR) {
-      L.lse(buf)[tb] = stl;
-      L.dl(buf)[tb] = std_;
-    }
-  }
-
-  __device__ __forceinline__ void write_tr() {
-    bf16* QT = L.qt();
-    bf16* OT = L.ot();
-#pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int gi = tb + g * G::NTB;
-      int qg, dg;
-      piece(gi, qg, dg);
-      const int pos = quad_pos(qg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // feature e of the four staged rows, as two packed pairs
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int wd = e >> 1;
-        u32x2 tq, to;
-        tq[0] = __builtin_amdgcn_perm(stq[g][1][wd], stq[g][0][wd], sel);
-        tq[1] = __builtin_amdgcn_perm(stq[g][3][wd], stq[g][2][wd], sel);
-        to[0] = __builtin_amdgcn_perm(sto[g][1][wd], sto[g][0][wd], sel);
-        to[1] = __builtin_amdgcn_perm(sto[g][3][wd], sto[g][2][wd], sel);
-        *(u32x2*)&QT[(dg * 8 + e) * G::BRP + pos] = tq;
-        *(u32x2*)&OT[(dg * 8 + e) * G::BRP + pos] = to;
-      }
-    }
   }
 
   __device__ __forceinline__ void read_ds() {
@@ -639,7 +634,7 @@ struct DqRole {
     }
   }
 
-  __device__ __forceinline__ void seg_begin(const Seg& sg) { stage_load(sg.bh, sub_row0(sg, 0)); }
+  __device__ __forceinline__ void seg_begin(const Seg& sg) { stage(sg.bh, sub_row0(sg, 0), 0); }
 
   __device__ __forceinline__ void seg_kd(const Seg&) {
     // K^T columns through the transpose read from the row-major K rows: lane i
@@ -658,9 +653,8 @@ struct DqRole {
   }
 
   __device__ __forceinline__ void seg_stage(const Seg& sg) {
-    write_rm(0);
-    write_tr();
-    if (sg.n > 1) stage_load(sg.bh, sub_row0(sg, 1));
+    stage_wait();  // sub-tile 0
+    if (sg.n > 1) stage(sg.bh, sub_row0(sg, 1), 1);
   }
 
   // The hand-off of sub-tile j runs in three steps spread over the next
@@ -788,27 +782,26 @@ struct DqRole {
   //            running-sum loads;
   //   interval j+2, after X:  add and store; hand over once the stores have
   //            completed, which the dQ MFMAs of j+1 leave time for.
-  // Before X a dQ wave only moves LDS data (dS of the previous sub-tile out,
-  // the transposed Q/dO of this one in) and starts the next staging loads.
-  // A wave hands sub-tile j over before it waits for its turn on j+1, so each
+  // Before X a dQ wave only reads the previous sub-tile's dS out of LDS and
+  // issues the DMA of the next sub-tile's rows. A wave hands sub-tile j over before it waits for its turn on j+1, so each
   // wait depends only on hand-overs that no later wait of their wave precedes:
   // with cyclic schedules (Shift, Symmetric Shift) this is what keeps the waits
   // free of cycles.
+  // The dQ waves also stage the query rows: sub-tile i+1 goes into the other
+  // buffer (its last readers passed the previous barrier Y) while sub-tile i
+  // is computed, and has landed before barrier Y.
   __device__ __forceinline__ void part1(const Seg& sg, int i) {
-    if (i > 0) {
-      read_ds();
-      write_tr();
-      if (i + 1 < sg.n) stage_load(sg.bh, sub_row0(sg, i + 1));
-    }
+    if (i > 0) read_ds();
+    if (i >= 1 && i + 1 < sg.n) stage(sg.bh, sub_row0(sg, i + 1), (i + 1) & 1);
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
     // (the running sums of i-2 were loaded an interval ago)
+    if (i + 1 < sg.n) stage_wait();   // sub-tile i+1's rows
     if (i > 1) commit();              // sub-tile i-2
     if (i > 0) dq_mma();              // sub-tile i-1
     release();                        // sub-tile i-2
     if (i > 0) acquire(sg, i - 1);    // sub-tile i-1
-    if (i + 1 < sg.n) write_rm((i + 1) & 1);
   }
 
   __device__ __forceinline__ void seg_end(const Seg& sg) {
