@@ -76,6 +76,20 @@ def draw(B: int, H: int, S: int, D: int, seed: int):
     return out
 
 
+def draw_grouped(B: int, H: int, Hkv: int, S: int, D: int, seed: int):
+    """Like draw, with K and V over Hkv heads (query heads sharing K/V heads).
+
+    Q and dO are [B, H, S, D], K and V [B, Hkv, S, D]; same dict keys as draw.
+    """
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = {}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv), ("do", H)):
+        t = torch.randn(B, heads, S, D, generator=g, dtype=torch.float32)
+        out[name + "32"] = t
+        out[name] = t.to(torch.bfloat16)
+    return out
+
+
 def draw_workload(w: Workload):
     return draw(w.B, w.H, w.S, w.D, w.seed)
 

@@ -68,6 +68,15 @@ def _check_qkv(*ts):
     return shape
 
 
+def _check_heads(q, k, v, *rest):
+    """q (and rest) [B, H, S, D], k and v [B, Hkv, S, D] with H % Hkv == 0; returns (B, H, Hkv, S, D)."""
+    B, H, S, D = _check_qkv(q, *rest)
+    Bk, Hkv, Sk, Dk = _check_qkv(k, v)
+    if (Bk, Sk, Dk) != (B, S, D) or Hkv <= 0 or H % Hkv:
+        raise ValueError(f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} (need [B, Hkv, S, D], H % Hkv == 0)")
+    return B, H, Hkv, S, D
+
+
 def _check_lse(lse, shape):
     torch = _torch()
     if lse.dtype != torch.float32 or lse.shape != shape[:3] or not lse.is_contiguous():
@@ -80,39 +89,51 @@ def tile(S: int, D: int, tile_request: int = 0) -> int:
     return t
 
 
-def workspace_size(B, H, S, D, causal, schedule="naive", tile_request=0) -> int:
-    n = _lib.load().attn_bwd_workspace_size(int(B), int(H), int(S), int(D), MASK_CAUSAL if causal else MASK_FULL,
-                                           _sched(schedule), int(tile_request))
+def workspace_size(B, H, S, D, causal, schedule="naive", tile_request=0, Hkv=None) -> int:
+    """Workspace bytes; Hkv = number of K/V heads when query heads share them (default H)."""
+    mask = MASK_CAUSAL if causal else MASK_FULL
+    if Hkv is None or int(Hkv) == int(H):
+        n = _lib.load().attn_bwd_workspace_size(int(B), int(H), int(S), int(D), mask, _sched(schedule),
+                                               int(tile_request))
+    else:
+        n = _lib.load().attn_bwd_gqa_workspace_size(int(B), int(H), int(Hkv), int(S), int(D), mask,
+                                                   _sched(schedule), int(tile_request))
     if n == 0:
         raise ValueError("invalid shape for the attention backward")
     return int(n)
 
 
-def alloc_workspace(B, H, S, D, causal, schedule="naive", tile_request=0, device="cuda"):
+def alloc_workspace(B, H, S, D, causal, schedule="naive", tile_request=0, device="cuda", Hkv=None):
     """Device workspace (uint8) for bwd/bwd_nondeterministic with these arguments."""
     torch = _torch()
-    return torch.empty(workspace_size(B, H, S, D, causal, schedule, tile_request), dtype=torch.uint8, device=device)
+    return torch.empty(workspace_size(B, H, S, D, causal, schedule, tile_request, Hkv), dtype=torch.uint8,
+                       device=device)
 
 
 def fwd(q, k, v, causal: bool, scale: float | None = None, out=None):
-    """Attention forward producing (O bf16 [B,H,S,D], LSE fp32 [B,H,S])."""
+    """Attention forward producing (O bf16 [B,H,S,D], LSE fp32 [B,H,S]); k, v may have fewer heads (grouped)."""
     torch = _torch()
-    B, H, S, D = _check_qkv(q, k, v)
+    B, H, Hkv, S, D = _check_heads(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    st = _lib.load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale,
-                              MASK_CAUSAL if causal else MASK_FULL, _stream_ptr(q.device))
+    mask = MASK_CAUSAL if causal else MASK_FULL
+    if Hkv == H:
+        st = _lib.load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, S, D, scale, mask,
+                                  _stream_ptr(q.device))
+    else:
+        st = _lib.load().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, S, D, scale, mask,
+                                      _stream_ptr(q.device))
     _lib.check(st, "attn_fwd")
     return o, lse
 
 
 def bwd(q, k, v, o, do, lse, causal: bool, schedule="naive", scale: float | None = None, tile_request: int = 0,
         workspace=None, out=None):
-    """Deterministic attention backward; returns (dq, dk, dv) bf16 [B,H,S,D]."""
+    """Deterministic attention backward; returns (dq, dk, dv) bf16 shaped like (q, k, v)."""
     return _bwd(q, k, v, o, do, lse, causal, _sched(schedule), scale, tile_request, workspace, out, True)
 
 
@@ -124,11 +145,11 @@ def bwd_nondeterministic(q, k, v, o, do, lse, causal: bool, scale: float | None 
 
 def _bwd(q, k, v, o, do, lse, causal, schedule, scale, tile_request, workspace, out, deterministic):
     torch = _torch()
-    B, H, S, D = _check_qkv(q, k, v, o, do)
+    B, H, Hkv, S, D = _check_heads(q, k, v, o, do)
     _check_lse(lse, q.shape)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if workspace is None:
-        workspace = alloc_workspace(B, H, S, D, causal, schedule, tile_request, q.device)
+        workspace = alloc_workspace(B, H, S, D, causal, schedule, tile_request, q.device, Hkv)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
@@ -136,7 +157,17 @@ def _bwd(q, k, v, o, do, lse, causal, schedule, scale, tile_request, workspace, 
     lib = _lib.load()
     mask = MASK_CAUSAL if causal else MASK_FULL
     stream = _stream_ptr(q.device)
-    if deterministic:
+    if Hkv != H:
+        if deterministic:
+            st = lib.attn_bwd_deterministic_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), mask,
+                                                schedule, _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, S, D, scale,
+                                                int(tile_request), _ptr(workspace), workspace.numel(), stream)
+        else:
+            st = lib.attn_bwd_nondeterministic_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), mask,
+                                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, S, D, scale,
+                                                   int(tile_request), _ptr(workspace), workspace.numel(), stream)
+        _lib.check(st, "attn_bwd_gqa")
+    elif deterministic:
         st = lib.attn_bwd_deterministic(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), mask, schedule,
                                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, S, D, scale, int(tile_request),
                                         _ptr(workspace), workspace.numel(), stream)

@@ -32,6 +32,10 @@ EXPORTS = (
     "attn_bwd_deterministic",
     "attn_bwd_nondeterministic",
     "attn_bwd_check",
+    "attn_fwd_gqa",
+    "attn_bwd_gqa_workspace_size",
+    "attn_bwd_deterministic_gqa",
+    "attn_bwd_nondeterministic_gqa",
     "attn_schedule_plan",
     "attn_debug_set_wait_limit",
     "attn_set_timing_events",
@@ -90,6 +94,16 @@ def _open(path: str) -> ctypes.CDLL:
     lib.attn_bwd_nondeterministic.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_bwd_nondeterministic.restype = i
     lib.attn_bwd_check.argtypes = [vp, sz, vp]
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd_gqa.restype = i
+    lib.attn_bwd_gqa_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_bwd_gqa_workspace_size.restype = sz
+    lib.attn_bwd_deterministic_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, i, i, i, i, f, i, vp,
+                                               sz, vp]
+    lib.attn_bwd_deterministic_gqa.restype = i
+    lib.attn_bwd_nondeterministic_gqa.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, f, i, vp,
+                                                  sz, vp]
+    lib.attn_bwd_nondeterministic_gqa.restype = i
     lib.attn_bwd_check.restype = i
     lib.attn_schedule_plan.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int32), sz, ctypes.POINTER(sz)]
     lib.attn_schedule_plan.restype = i

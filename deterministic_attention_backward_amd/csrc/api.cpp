@@ -35,12 +35,14 @@ int choose_tile(int S, int D, int tile_request) {
 struct Shape {
   int T, BR, N, S_pad, n_qsub;
   long long BH;
+  bool grouped;  // fewer K/V heads than query heads
 };
 
 // Shape checks shared by the backward entry points; returns a status.
-int check_shape(int B, int H, int S, int D, int mask, int schedule, int tile_request, bool deterministic,
+int check_shape(int B, int H, int Hkv, int S, int D, int mask, int schedule, int tile_request, bool deterministic,
                 Shape* sh) {
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (mask != ATTN_MASK_FULL && mask != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (schedule < ATTN_SCHED_NAIVE || schedule > ATTN_SCHED_SYMMETRIC_SHIFT) return ATTN_ERR_INVALID_ARG;
   if (tile_request != 0 && tile_request != 64 && tile_request != 128) return ATTN_ERR_INVALID_ARG;
@@ -62,12 +64,13 @@ int check_shape(int B, int H, int S, int D, int mask, int schedule, int tile_req
   sh->S_pad = static_cast<int>(N * T);
   sh->n_qsub = static_cast<int>(N * (T / BR));
   sh->BH = BH;
+  sh->grouped = Hkv != H;
   return ATTN_OK;
 }
 
 WsLayout layout_for(const Shape& sh, int D, int schedule, bool deterministic) {
   const bool park = deterministic && schedule == ATTN_SCHED_SYMMETRIC_SHIFT;
-  return ws_layout(sh.BH, sh.S_pad, D, sh.n_qsub, sh.T, park);
+  return ws_layout(sh.BH, sh.S_pad, D, sh.n_qsub, sh.T, park, sh.grouped);
 }
 
 int num_cu_current(int* out) {
@@ -85,12 +88,12 @@ int num_cu_current(int* out) {
 }
 
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-            int mask, int schedule, void* dq, void* dk, void* dv, int B, int H, int S, int D, float scale,
+            int mask, int schedule, void* dq, void* dk, void* dv, int B, int H, int Hkv, int S, int D, float scale,
             int tile_request, void* workspace, size_t workspace_bytes, void* stream, bool deterministic) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   Shape sh;
-  const int st = check_shape(B, H, S, D, mask, schedule, tile_request, deterministic, &sh);
+  const int st = check_shape(B, H, Hkv, S, D, mask, schedule, tile_request, deterministic, &sh);
   if (st != ATTN_OK) return st;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
   for (const void* ptr : ptrs)
@@ -106,7 +109,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.ws = static_cast<char*>(workspace);
   a.lay = lay;
-  a.B = B; a.H = H; a.S = S; a.D = D;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.S = S; a.D = D;
   a.T = sh.T; a.BR = sh.BR; a.N = sh.N; a.S_pad = sh.S_pad; a.n_qsub = sh.n_qsub;
   a.scale = scale;
   a.causal = mask == ATTN_MASK_CAUSAL;
@@ -141,8 +144,14 @@ const char* attn_status_string(int status) {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int S, int D,
              float scale, int mask, void* stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, S, D, scale, mask, stream);
+}
+
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int S,
+                 int D, float scale, int mask, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || S <= 0 || D <= 0 || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || S <= 0 || D <= 0 || !std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (mask != ATTN_MASK_FULL && mask != ATTN_MASK_CAUSAL) return ATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (static_cast<long long>(B) * H > 65535 || static_cast<long long>(B) * H * S * D >= (1ll << 40))
@@ -152,7 +161,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (!aligned16(ptr)) return ATTN_ERR_ALIGNMENT;
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.B = B; a.H = H; a.S = S; a.D = D;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.S = S; a.D = D;
   a.causal = mask == ATTN_MASK_CAUSAL;
   a.scale = scale;
   return launch_fwd(a, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -166,10 +175,14 @@ int attn_bwd_tile(int S, int D, int tile_request) {
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int S, int D, int mask, int schedule, int tile_request) {
+  return attn_bwd_gqa_workspace_size(B, H, H, S, D, mask, schedule, tile_request);
+}
+
+size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int S, int D, int mask, int schedule, int tile_request) {
   Shape sh;
-  if (check_shape(B, H, S, D, mask, schedule, tile_request, true, &sh) != ATTN_OK) {
+  if (check_shape(B, H, Hkv, S, D, mask, schedule, tile_request, true, &sh) != ATTN_OK) {
     // the non-deterministic call accepts any schedule value; size it as NAIVE
-    if (check_shape(B, H, S, D, mask, ATTN_SCHED_NAIVE, tile_request, true, &sh) != ATTN_OK) return 0;
+    if (check_shape(B, H, Hkv, S, D, mask, ATTN_SCHED_NAIVE, tile_request, true, &sh) != ATTN_OK) return 0;
     return layout_for(sh, D, ATTN_SCHED_NAIVE, true).total;
   }
   return layout_for(sh, D, schedule, true).total;
@@ -179,15 +192,31 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
                            const float* lse, int mask, int schedule, void* dq, void* dk, void* dv, int B, int H,
                            int S, int D, float scale, int tile_request, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  return run_bwd(q, k, v, o, dout, lse, mask, schedule, dq, dk, dv, B, H, S, D, scale, tile_request, workspace,
+  return run_bwd(q, k, v, o, dout, lse, mask, schedule, dq, dk, dv, B, H, H, S, D, scale, tile_request, workspace,
                  workspace_bytes, stream, true);
+}
+
+int attn_bwd_deterministic_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, int mask, int schedule, void* dq, void* dk, void* dv, int B, int H,
+                               int Hkv, int S, int D, float scale, int tile_request, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return run_bwd(q, k, v, o, dout, lse, mask, schedule, dq, dk, dv, B, H, Hkv, S, D, scale, tile_request,
+                 workspace, workspace_bytes, stream, true);
 }
 
 int attn_bwd_nondeterministic(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, int mask, void* dq, void* dk, void* dv, int B, int H, int S, int D,
                               float scale, int tile_request, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  return run_bwd(q, k, v, o, dout, lse, mask, ATTN_SCHED_NAIVE, dq, dk, dv, B, H, S, D, scale, tile_request,
+  return run_bwd(q, k, v, o, dout, lse, mask, ATTN_SCHED_NAIVE, dq, dk, dv, B, H, H, S, D, scale, tile_request,
+                 workspace, workspace_bytes, stream, false);
+}
+
+int attn_bwd_nondeterministic_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                  const float* lse, int mask, void* dq, void* dk, void* dv, int B, int H, int Hkv,
+                                  int S, int D, float scale, int tile_request, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return run_bwd(q, k, v, o, dout, lse, mask, ATTN_SCHED_NAIVE, dq, dk, dv, B, H, Hkv, S, D, scale, tile_request,
                  workspace, workspace_bytes, stream, false);
 }
 

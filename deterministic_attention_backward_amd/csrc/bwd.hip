@@ -128,6 +128,8 @@ struct MainParams {
   bf16* dq;
   int *flags, *header, *heads;
   int S, S_pad, N, n_qsub, n_workers, n_units, sched, BH;
+  int H, group;  // query heads per batch; query heads per K/V head
+  float* dkv;    // group > 1: per query head fp32 dK (scaled), then dV, [BH][S_pad][D] each
   int flag_stride, heads_row;  // int32 elements per head of flags / per queue row of heads
   int poison_flag;             // >= 0: the wait on this flag can never succeed (exercises the bound)
   float scale, scale_log2;
@@ -353,8 +355,10 @@ struct TileRole {
   __device__ __forceinline__ void seg_begin(const Seg& sg) {
     const int S = p.S;
     const int key = min(sg.kv * G::T + 32 * a + l32, S - 1);  // keys past the end are masked
-    const bf16* kh = p.k + (size_t)sg.bh * S * G::D;
-    const bf16* vh = p.v + (size_t)sg.bh * S * G::D;
+    // K/V head of this query head (grouped-query attention: group consecutive query heads share one)
+    const int kvh = (sg.bh / p.H) * (p.H / p.group) + (sg.bh % p.H) / p.group;
+    const bf16* kh = p.k + (size_t)kvh * S * G::D;
+    const bf16* vh = p.v + (size_t)kvh * S * G::D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const unsigned off = 2u * (unsigned)(key * G::D + 16 * c + 8 * hh);
@@ -522,6 +526,21 @@ struct TileRole {
       return;
     }
     const int S = p.S;
+    if (p.dkv) {  // grouped-query heads: this query head's share, summed over the group later
+      float* pk = p.dkv + (size_t)sg.bh * p.S_pad * G::D;
+      float* pv = pk + (size_t)p.BH * p.S_pad * G::D;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = sg.kv * G::T + 32 * a + 8 * (i / 4) + 4 * hh + (i % 4);
+          const size_t off = (size_t)key * G::D + 32 * n + l32;  // key < S_pad
+          pk[off] = dKa[n][i] * p.scale;
+          pv[off] = dVa[n][i];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
 #pragma unroll
@@ -995,6 +1014,42 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
 // --------------------------------------------------------------------------------------
 // launcher
 
+// --------------------------------------------------------------------------------------
+// grouped-query epilogue: dK, dV of K/V head hk = the sum over its G query heads
+// hk G, ..., hk G + G - 1, added in that order (a fixed order: deterministic)
+
+__global__ void __launch_bounds__(256) bwd_gqa_reduce_kernel(const float* dkv, bf16* dk, bf16* dv, int H, int Hkv,
+                                                             int S, int S_pad, int D, long long BH) {
+  const int G = H / Hkv;
+  const long long quads = (long long)(BH / H) * Hkv * S * (D / 4);  // output elements / 4
+  const long long part = BH * S_pad * D;                             // floats per tensor of dkv
+  const long long nthreads = (long long)gridDim.x * blockDim.x;
+  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < quads; t += nthreads) {
+    const long long e = t * 4;                   // output element: ((b Hkv + hk) S + s) D + d
+    const long long row = e / D;                 // (b Hkv + hk) S + s
+    const int d = (int)(e - row * D);
+    const long long bk = row / S;                // b Hkv + hk
+    const int s = (int)(row - bk * S);
+    const long long b = bk / Hkv, hk = bk - b * Hkv;
+    const long long h0 = b * H + hk * G;         // first query head of the group
+    f32x4 ak = {0.0f, 0.0f, 0.0f, 0.0f}, av = ak;
+    for (int g = 0; g < G; ++g) {
+      const long long src = ((h0 + g) * S_pad + s) * D + d;
+      const f32x4 xk = *(const f32x4*)(dkv + src);
+      const f32x4 xv = *(const f32x4*)(dkv + part + src);
+      ak += xk;
+      av += xv;
+    }
+    bf16x4 ok, ov;
+    for (int k = 0; k < 4; ++k) {
+      ok[k] = to_bf16(ak[k]);
+      ov[k] = to_bf16(av[k]);
+    }
+    *(bf16x4*)(dk + e) = ok;
+    *(bf16x4*)(dv + e) = ov;
+  }
+}
+
 template <int D, int T, int BR, bool CAUSAL, int MODE>
 static hipError_t launch_main(const MainParams& mp, int grid, hipStream_t stream) {
   g_last_grid = grid;
@@ -1090,6 +1145,9 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.heads = heads;
   mp.dq = (bf16*)a.dq;
   mp.BH = (int)BH;
+  mp.H = a.H;
+  mp.group = a.H / a.Hkv;
+  mp.dkv = mp.group > 1 ? (float*)(a.ws + a.lay.dkv) : nullptr;
   mp.S = a.S;
   mp.S_pad = a.S_pad;
   mp.N = a.N;
@@ -1126,6 +1184,13 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
     else
       hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
                          a.S_pad, a.BR, atomic ? 0 : 1, a.scale);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && mp.group > 1) {
+    const long long want = ((long long)a.B * a.Hkv * a.S * (a.D / 4) + 255) / 256;
+    const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+    hipLaunchKernelGGL(bwd_gqa_reduce_kernel, dim3(g), dim3(256), 0, stream, (const float*)mp.dkv, (bf16*)a.dk,
+                       (bf16*)a.dv, a.H, a.Hkv, a.S, a.S_pad, a.D, BH);
     e = hipGetLastError();
   }
   return e;

@@ -17,6 +17,7 @@ struct FwdParams {
   bf16* o;
   float* lse;
   int S;
+  int H, group;  // query heads per batch; query heads per K/V head
   float scale_log2;
 };
 
@@ -36,8 +37,9 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
   const int q0 = blockIdx.x * 128;
   const int qrow = q0 + 32 * w + l32;   // this lane's query
   const bf16* qh = p.q + bh * S * D;
-  const bf16* kh = p.k + bh * S * D;
-  const bf16* vh = p.v + bh * S * D;
+  const long long kvh = (bh / p.H) * (p.H / p.group) + (bh % p.H) / p.group;  // this query head's K/V head
+  const bf16* kh = p.k + kvh * S * D;
+  const bf16* vh = p.v + kvh * S * D;
 
   bf16x8 Qr[KC];
 #pragma unroll
@@ -164,6 +166,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   fp.o = (bf16*)a.o;
   fp.lse = a.lse;
   fp.S = a.S;
+  fp.H = a.H;
+  fp.group = a.H / a.Hkv;
   fp.scale_log2 = a.scale * 1.4426950408889634f;
   const dim3 grid((unsigned)((a.S + 127) / 128), (unsigned)((long long)a.B * a.H));
   if (a.D == 64) {

@@ -32,8 +32,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //   dq_ws    fp32[BH * S_pad * D]: dQ accumulator
 //   park     fp32[kMaxGrid * 2 * T * D * 2]: Symmetric Shift only; per workgroup,
 //            one slot per KV tile of its pair, each holding dK and dV
+//   dkv      fp32[2][BH * S_pad * D]: grouped-query heads only; each query
+//            head's dK (scaled) and dV, summed over the group afterwards
 struct WsLayout {
-  size_t header, heads, flags, lse2, delta, dq_ws, park, total;
+  size_t header, heads, flags, lse2, delta, dq_ws, park, dkv, total;
   long long heads_row, flag_stride;  // int32 elements per queue row / per head
 };
 
@@ -42,7 +44,7 @@ inline int dq_waves(int T) { return T / 32; }
 
 inline long long align64(long long x) { return (x + 63) & ~63ll; }
 
-inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, bool park) {
+inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, bool park, bool grouped) {
   WsLayout w;
   w.heads_row = align64(BH);
   w.flag_stride = align64((long long)n_qsub * dq_waves(T));
@@ -54,6 +56,7 @@ inline WsLayout ws_layout(long long BH, int S_pad, int D, int n_qsub, int T, boo
   w.delta = off;    off += align256(size_t(BH) * S_pad * sizeof(float));
   w.dq_ws = off;    off += align256(size_t(BH) * S_pad * D * sizeof(float));
   w.park = off;     off += park ? align256(size_t(kMaxGrid) * 2 * T * D * 2 * sizeof(float)) : 0;
+  w.dkv = off;      off += grouped ? 2 * align256(size_t(BH) * S_pad * D * sizeof(float)) : 0;
   w.total = off;
   return w;
 }
@@ -64,7 +67,7 @@ struct BwdArgs {
   void *dq, *dk, *dv;
   char* ws;
   WsLayout lay;
-  int B, H, S, D, T, BR, N, S_pad, n_qsub;
+  int B, H, Hkv, S, D, T, BR, N, S_pad, n_qsub;  // Hkv: K/V heads (H / Hkv query heads share one)
   float scale;
   int causal, sched, atomic;
   uint32_t wait_limit;
@@ -77,7 +80,7 @@ struct FwdArgs {
   const void *q, *k, *v;
   void* o;
   float* lse;
-  int B, H, S, D, causal;
+  int B, H, Hkv, S, D, causal;
   float scale;
 };
 

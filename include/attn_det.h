@@ -138,6 +138,37 @@ int attn_bwd_nondeterministic(const void* q, const void* k, const void* v, const
 int attn_bwd_check(const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Grouped-query attention (query heads sharing K/V heads). Not on the pages:
+ * the end-to-end models they time share K/V heads across query heads in some
+ * configurations, which needs a second fixed-order reduction (dK, dV over the
+ * query heads of a group). H query heads, Hkv K/V heads, H % Hkv == 0, and
+ * query head h uses K/V head h / (H / Hkv) (consecutive query heads share
+ * one). q, o, dout, dq: bf16 [B][H][S][D]; lse: fp32 [B][H][S]; k, v, dk,
+ * dv: bf16 [B][Hkv][S][D]. Hkv == H is the plain call. The backward computes
+ * each query head's dK (scaled) and dV in fp32 as the plain call does, then
+ * sums them over the group in the fixed order of the query heads and rounds
+ * once to bf16, so it is bit-reproducible like the plain call. Everything
+ * else (masks, schedules, tiles, workspace ownership, status codes) is as for
+ * the plain calls; the workspace is sized by attn_bwd_gqa_workspace_size and
+ * holds two more fp32 [B][H][S_pad][D] tensors when Hkv < H. H % Hkv != 0 is
+ * ATTN_ERR_INVALID_ARG.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int S, int D, float scale, int mask, void* stream);
+size_t attn_bwd_gqa_workspace_size(int B, int H, int Hkv, int S, int D, int mask, int schedule,
+                                   int tile_request);
+int attn_bwd_deterministic_gqa(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, int mask, int schedule,
+                               void* dq, void* dk, void* dv, int B, int H, int Hkv, int S, int D,
+                               float scale, int tile_request, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int attn_bwd_nondeterministic_gqa(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, int mask,
+                                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int S, int D,
+                                  float scale, int tile_request, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * attn_schedule_plan - host-only export of one head's schedule (no HIP call).
  *   n_tiles = N; mask, schedule as above.
  *   Writes int32 values to out: [n_workers, n_tasks, then for every task, in

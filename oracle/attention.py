@@ -201,3 +201,57 @@ def backward_rows_head(q, k, v, o, do, lse, causal: bool, scale: float, q_rows, 
     dv = p_k.T @ do
     dk = scale * (ds_k.T @ q)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Grouped-query attention (query heads sharing K/V heads). Not on the pages:
+# the end-to-end models they time are of a family that shares K/V heads across
+# query heads, which asks for a second fixed-order reduction of dK/dV. With H
+# query heads and Hkv K/V heads (G = H / Hkv), query head h attends with K/V
+# head h // G. Each query head is ordinary attention with that K and V, so the
+# forward is the per-head definition above; a K/V head is used by G query
+# heads, so by the chain rule its gradient is the sum of the G per-use
+# gradients (dK, dV of each query head taken with respect to its copy).
+
+
+def group_of(H: int, Hkv: int, h: int) -> int:
+    """K/V head of query head h (consecutive query heads share one)."""
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    return h // (H // Hkv)
+
+
+def forward_grouped(q, k, v, causal: bool, scale: float, row_block: int = ROW_BLOCK):
+    """q [B,H,S,D], k, v [B,Hkv,S,D] -> (O [B,H,S,D], LSE [B,H,S])."""
+    B, H, S, D = q.shape
+    Hkv = k.shape[1]
+    o = np.empty((B, H, S, v.shape[-1]))
+    lse = np.empty((B, H, S))
+    for b in range(B):
+        for h in range(H):
+            g = group_of(H, Hkv, h)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], causal, scale, row_block)
+    return o, lse
+
+
+def backward_grouped(q, k, v, o, do, lse, causal: bool, scale: float, row_block: int = ROW_BLOCK):
+    """Gradients for shared K/V heads: dQ [B,H,S,D]; dK, dV [B,Hkv,S,D] summed over each group."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = group_of(H, Hkv, h)
+            dq[b, h], dkh, dvh = backward_head(q[b, h], k[b, g], v[b, g], o[b, h], do[b, h], lse[b, h], causal,
+                                              scale, row_block)
+            dk[b, g] += dkh
+            dv[b, g] += dvh
+    return dq, dk, dv
+
+
+def loss_grouped(q, k, v, do, causal: bool, scale: float):
+    """The scalar sum(O * dO) with shared K/V heads (its gradient is backward_grouped's)."""
+    o, _ = forward_grouped(q, k, v, causal, scale)
+    return float((o * do).sum())

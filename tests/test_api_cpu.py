@@ -116,6 +116,32 @@ def test_fwd_validation():
                         None) == _lib.ERR_ALIGNMENT
 
 
+def call_gqa(**over):
+    lib = _lib.load()
+    p = FakePtr()
+    args = dict(q=p(1), k=p(2), v=p(3), o=p(4), dout=p(5), lse=p(6), mask=0, schedule=0, dq=p(7), dk=p(8),
+                dv=p(9), B=1, H=4, Hkv=2, S=256, D=64, scale=0.125, tile=0, ws=p(10), ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return lib.attn_bwd_deterministic_gqa(*args.values())
+
+
+def test_grouped_validation_and_workspace():
+    lib = _lib.load()
+    assert call_gqa(Hkv=3) == _lib.ERR_INVALID_ARG          # 4 query heads cannot share 3 K/V heads evenly
+    assert call_gqa(Hkv=0) == _lib.ERR_INVALID_ARG
+    assert call_gqa(dk=None) == _lib.ERR_INVALID_ARG
+    assert call_gqa(D=96) == _lib.ERR_UNSUPPORTED
+    assert call_gqa(ws_bytes=1024) == _lib.ERR_WORKSPACE
+    p = FakePtr()
+    assert lib.attn_fwd_gqa(p(0), p(1), p(2), p(3), p(4), 1, 4, 3, 64, 64, 0.1, 0, None) == _lib.ERR_INVALID_ARG
+    assert lib.attn_bwd_gqa_workspace_size(1, 6, 4, 256, 64, 0, 0, 0) == 0
+    # sharing K/V heads adds the per-query-head fp32 dK and dV (two [B, H, S_pad, D] tensors)
+    B, H, S, D = 2, 8, 1000, 128
+    plain = lib.attn_bwd_gqa_workspace_size(B, H, H, S, D, 1, 2, 0)
+    assert plain == lib.attn_bwd_workspace_size(B, H, S, D, 1, 2, 0)
+    assert lib.attn_bwd_gqa_workspace_size(B, H, 2, S, D, 1, 2, 0) >= plain + 2 * B * H * 1024 * D * 4
+
+
 def plan_cases():
     for N in (1, 2, 3, 4, 5, 6, 8, 16, 31, 32, 64, 128):
         yield N, False, Sch.NAIVE
