@@ -32,6 +32,11 @@ class Workload:
     seed: int
     tile: int = 0  # 0 = let the library choose the KV/Q tile edge
     note: str = ""
+    Hkv: int = 0   # K/V heads when query heads share them (0: one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -45,7 +50,8 @@ class Workload:
 
     def describe(self) -> str:
         mask = "causal" if self.causal else "full"
-        return f"B={self.B},H={self.H},S={self.S},D={self.D},{mask}"
+        kv = f",Hkv={self.Hkv}" if self.Hkv and self.Hkv != self.H else ""
+        return f"B={self.B},H={self.H}{kv},S={self.S},D={self.D},{mask}"
 
 
 # The pages give no shapes; these stand in for their workloads (head shapes of
@@ -58,6 +64,8 @@ WORKLOADS = {
     "C3F": Workload("C3F", 4, 32, 4096, 128, False, 3, note="C3's shape with a full mask"),
     "C4": Workload("C4", 2, 16, 8192, 64, True, 4),
     "C5": Workload("C5", 1, 16, 16384, 128, False, 5, note="long-sequence full mask"),
+    "C3G": Workload("C3G", 4, 32, 4096, 128, True, 3, Hkv=8,
+                    note="C3 with 8 shared K/V heads (grouped-query attention of 8B-class models)"),
 }
 
 
@@ -91,6 +99,8 @@ def draw_grouped(B: int, H: int, Hkv: int, S: int, D: int, seed: int):
 
 
 def draw_workload(w: Workload):
+    if w.kv_heads != w.H:
+        return draw_grouped(w.B, w.H, w.kv_heads, w.S, w.D, w.seed)
     return draw(w.B, w.H, w.S, w.D, w.seed)
 
 

@@ -138,8 +138,10 @@ def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
     t0 = time.perf_counter()
     while heads < B * H:
         b, h = divmod(heads, H)
-        f = lambda t: t[b, h].to(dtype=__import__("torch").float64).numpy()
-        q, k, v, do = (f(inputs[n]) for n in ("q", "k", "v", "do"))
+        f = lambda t, hh=h: t[b, hh].to(dtype=__import__("torch").float64).numpy()
+        hk = h // (H // w.kv_heads)  # the query head's K/V head (grouped-query workloads)
+        q, do = f(inputs["q"]), f(inputs["do"])
+        k, v = f(inputs["k"], hk), f(inputs["v"], hk)
         A.backward_head(q, k, v, f(o_cpu), do, lse_cpu[b, h].double().numpy(), w.causal, w.scale)
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -168,7 +170,7 @@ def wait_profile(w, sched, args, torch, dab, _lib, tensors):
     try:
         _lib._lib = prof
         dab.set_dq_protocol(args.dq_protocol)
-        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, sched, w.tile)
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, sched, w.tile, Hkv=w.kv_heads)
         for _ in range(2):
             dab.bwd(q, k, v, o, do, lse, w.causal, sched, w.scale, w.tile, ws)
         torch.cuda.synchronize()
@@ -233,11 +235,11 @@ def main():
         scheds = args.schedules.split(",")
     else:
         scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else [])
-    out = tuple(torch.empty_like(q) for _ in range(3))
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     results = {}
     dab.wait_timeouts(reset=True)
     for s in scheds:
-        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile)
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile, Hkv=w.kv_heads)
         fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
         ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
         dab.check_workspace(ws)
@@ -249,7 +251,7 @@ def main():
         del ws
     nondet = None
     if not args.no_nondet:
-        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile)
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile, Hkv=w.kv_heads)
         fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
         ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
         nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
