@@ -189,6 +189,67 @@ def wait_profile(w, sched, args, torch, dab, _lib, tensors):
             "note": "s_memtime cycles of one tile wave and one dQ wave per workgroup, profiling build"}
 
 
+def block_bench(args):
+    """One forward + backward step of an 8B-class attention block (random weights), deterministic
+    attention backward against the atomic-dQ one; prints its own JSON line."""
+    import torch
+    import deterministic_attention_backward_amd as dab
+    from deterministic_attention_backward_amd.autograd import AttentionBlock
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible: the benchmark needs an MI355X")
+    B, S, hidden, heads, kv_heads, D = 1, 8192, 4096, 32, 8, 128
+    log(f"attention block: B={B} S={S} hidden={hidden} heads={heads} kv_heads={kv_heads} head_dim={D} causal")
+    g = torch.Generator(device="cpu").manual_seed(9)
+    x0 = torch.randn(B, S, hidden, generator=g).to(torch.bfloat16).cuda()
+    dy = torch.randn(B, S, hidden, generator=g).to(torch.bfloat16).cuda()
+    res = {}
+    for name, sched in (("deterministic", "shift"), ("atomic", None)):
+        block = AttentionBlock(hidden, heads, kv_heads, D, causal=True, schedule=sched, seed=1)
+
+        def step():
+            block.zero_grad(set_to_none=True)
+            x = x0.detach().requires_grad_()
+            block(x).backward(dy)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / args.steps * 1e3
+        log(f"  {name:14s} {res[name]:8.3f} ms per block step ({B * S / res[name] * 1e3:,.0f} tokens/s)")
+    # the attention backward alone on the block's shapes (deterministic, Shift)
+    x = {n: torch.randn(*shape, generator=g).to(torch.bfloat16).cuda()
+         for n, shape in (("q", (B, heads, S, D)), ("k", (B, kv_heads, S, D)), ("v", (B, kv_heads, S, D)),
+                          ("do", (B, heads, S, D)))}
+    o, lse = dab.fwd(x["q"], x["k"], x["v"], True)
+    ws = dab.alloc_workspace(B, heads, S, D, True, "shift", 0, Hkv=kv_heads)
+    fn = lambda: dab.bwd(x["q"], x["k"], x["v"], o, x["do"], lse, True, "shift", workspace=ws)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    attn_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    log(f"  attention backward alone (deterministic, Shift): {attn_ms:.3f} ms")
+    line = {"metric": "attention block step (forward + backward), 8B-class shape", "value": round(B * S / res["deterministic"] * 1e3, 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(res["deterministic"], 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random weights and inputs)",
+            "config": {"workload": f"attention block: B={B},S={S},hidden={hidden},heads={heads},kv_heads={kv_heads},"
+                                   f"D={D},causal", "schedule": "shift"},
+            "atomic_ms_per_step": round(res["atomic"], 4),
+            "deterministic_over_atomic_step_time": round(res["deterministic"] / res["atomic"], 4),
+            "attention_backward_ms": round(attn_ms, 4),
+            "attention_backward_share": round(attn_ms / res["deterministic"], 4)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +262,8 @@ def main():
                     help="dQ hand-off of the deterministic calls (auto picks XCD-local where it applies)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle leg (0 = skip)")
     ap.add_argument("--no-mfma-probe", action="store_true", help="skip the measured-MFMA-peak probe")
+    ap.add_argument("--block", action="store_true",
+                    help="time an 8B-class attention block (forward + backward) instead; prints its own JSON line")
     ap.add_argument("--wait-profile", action="store_true",
                     help="one extra, untimed call of the best schedule with the profiling build: wait-cycle fractions")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +274,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.block:
+        block_bench(args)
+        return
 
     import torch
     import attn_inputs
