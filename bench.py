@@ -98,7 +98,7 @@ def time_variant(fn, steps, warmup, torch, events, lib):
     return wall / steps * 1e3, sum(kern) / len(kern), {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
 
 
-KERNEL_SOURCES = ("bwd.hip", "common.hpp", "schedule.hpp", "launch.hpp")
+KERNEL_SOURCES = ("bwd.hip", "common.hpp", "lds.hpp", "schedule.hpp", "launch.hpp")
 
 
 def measured_traffic(workload: str, schedule: str, protocol: str):

@@ -18,6 +18,7 @@
 #include "../../include/attn_det.h"
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds.hpp"
 #include "schedule.hpp"
 
 namespace attn {
@@ -178,32 +179,6 @@ __device__ __forceinline__ f32x4 sys_load16(const float* base, unsigned bytes, u
 __device__ __forceinline__ void sys_store16(float* base, unsigned bytes, unsigned byte_off, f32x4 v) {
   typedef unsigned u32v4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32v4, v), rsrc(base, bytes), (int)byte_off, 0, 17);
-}
-
-// Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
-// supplies the address of a 4-element row chunk and receives element i % 4 of
-// the chunks supplied by lanes 4e + i / 4, e = 0..3.
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s4*)(__attribute__((address_space(3))) char*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
-// Staged query rows (Q, dO) hold D bf16 without padding, in 16-byte chunks;
-// chunk c of row r sits at position c ^ swz(r). With 64 LDS banks of 4 bytes,
-// a 16-byte read serves 16 lanes per pass and an 8-byte read 32 lanes:
-//  - row-wise reads (16 consecutive rows, one chunk each) land on 16
-//    different positions (D = 128: 256-byte rows, swz bijective on r mod 16;
-//    D = 64: 128-byte rows, swz bijective on the even and on the odd rows);
-//  - transposed reads (4 consecutive rows, 4 consecutive chunks of an aligned
-//    group) land on 16 different positions, because swz gives 4 consecutive
-//    rows (D = 64: the two of each parity) different bits above the two lowest.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(D == 64 || D == 128, "head dims");
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Workgroup barrier over LDS only: this wave's LDS operations complete
