@@ -293,9 +293,15 @@ struct Seg {
 
 // ---- tile waves
 
+#ifndef ATTN_TILE_PIPE
+#define ATTN_TILE_PIPE 1
+#endif
+
 template <class G, bool CAUSAL, int MODE>
 struct TileRole {
   static constexpr int KC = G::KC, ND = G::ND, MB = G::MB, NSUB = G::NSUB;
+  // software-pipelined row blocks (D = 64: registers to spare for a second S/dP block)
+  static constexpr bool PIPE = ATTN_TILE_PIPE != 0 && G::D == 64;
   const MainParams& p;
   Lds<G> L;
   int tid, lane, a, l32, hh;
@@ -378,6 +384,12 @@ struct TileRole {
 
   // S and dP of row block m, turned into P and dS in place
   __device__ __forceinline__ void sdp(int m, int buf, int q_base, int kv_base, bool need_mask) {
+    mma(m, buf, s, dp);
+    soft(m, buf, q_base, kv_base, need_mask, s, dp);
+  }
+
+  // S and dP of row block m (raw scores)
+  __device__ __forceinline__ void mma(int m, int buf, f32x16& s, f32x16& dp) {
     // (the lane constants are re-read here so that the compiler computes the
     // swizzled addresses where they are used instead of keeping them all live)
     int ab = a_base, s1 = sw1;
@@ -403,8 +415,13 @@ struct TileRole {
       }
       s = mfma32(qa[c & 1], Kr[c], s);
       dp = mfma32(oa[c & 1], VL ? vb[c & 1] : Vr[VL ? 0 : c], dp);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // P = exp2(S scale log2(e) - LSE log2(e)) and dS = P (dP - Delta), in place
+  __device__ __forceinline__ void soft(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
+                                       f32x16& dp) {
     const float* Ls = L.lse(buf);
     const float* Ds = L.dl(buf);
     const int key_g = kv_base + 32 * a + l32;
@@ -450,8 +467,9 @@ struct TileRole {
   }
 
   __device__ __forceinline__ void accumulate(int m, int buf) {
-    const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 8);
-    const bf16x8 db0 = pack8(dp, 0), db1 = pack8(dp, 8);
+    accumulate(m, buf, pack8(s, 0), pack8(s, 8), pack8(dp, 0), pack8(dp, 8));
+  }
+  __device__ __forceinline__ void accumulate(int m, int buf, bf16x8 pb0, bf16x8 pb1, bf16x8 db0, bf16x8 db1) {
     bf16* drow = &L.dst()[(32 * a + l32) * G::SP + 32 * m + 4 * hh];  // four consecutive queries per write
     *(bf16x4*)(drow + 0) = __builtin_shufflevector(db0, db0, 0, 1, 2, 3);
     *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
@@ -482,7 +500,7 @@ struct TileRole {
       dVa[n] = mfma32(pb1, ov[n & 1][1], dVa[n]);
       dKa[n] = mfma32(db0, qv[n & 1][0], dKa[n]);
       dKa[n] = mfma32(db1, qv[n & 1][1], dKa[n]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -504,11 +522,32 @@ struct TileRole {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    accumulate(0, i & 1);
+    if constexpr (PIPE) {
+      // row block m+1's scores are issued before row block m's dV/dK
+      // products, and its softmax follows them: with no scheduling fences the
+      // compiler can interleave one block's VALU work with the other's MFMAs
+      // (a finished block is kept packed to bf16, as the MFMAs take it)
+      bf16x8 pk[4] = {pack8(s, 0), pack8(s, 8), pack8(dp, 0), pack8(dp, 8)};
 #pragma unroll
-    for (int m = 1; m < MB; ++m) {
-      sdp(m, i & 1, q_base, kv_base, need_mask);
-      accumulate(m, i & 1);
+      for (int m = 0; m < MB; ++m) {
+        f32x16 sn, dn;
+        if (m + 1 < MB) mma(m + 1, i & 1, sn, dn);
+        accumulate(m, i & 1, pk[0], pk[1], pk[2], pk[3]);
+        if (m + 1 < MB) {
+          soft(m + 1, i & 1, q_base, kv_base, need_mask, sn, dn);
+          pk[0] = pack8(sn, 0);
+          pk[1] = pack8(sn, 8);
+          pk[2] = pack8(dn, 0);
+          pk[3] = pack8(dn, 8);
+        }
+      }
+    } else {
+      accumulate(0, i & 1);
+#pragma unroll
+      for (int m = 1; m < MB; ++m) {
+        sdp(m, i & 1, q_base, kv_base, need_mask);
+        accumulate(m, i & 1);
+      }
     }
   }
 
