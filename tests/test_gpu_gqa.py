@@ -95,20 +95,25 @@ def schedules(S, D, causal):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dKV%dS%dD%d%s" % (c[0], c[1], c[2], c[3], c[4],
                                                                               "c" if c[5] else "f"))
-def test_grouped_forward_and_backward_parity(case):
+@pytest.mark.parametrize("protocol", ["auto", "device"])
+def test_grouped_forward_and_backward_parity(case, protocol):
     B, H, Hkv, S, D, causal, seed = case
-    say(f"grouped parity {case}")
+    say(f"grouped parity {case} dq protocol={protocol}")
     c = GCase(B, H, Hkv, S, D, causal, seed)
     o_ref, lse_ref = A.forward_grouped(c.nq, c.nk, c.nv, causal, c.scale)
     assert_close("O", c.no, o_ref)
     assert np.abs(c.nlse - lse_ref).max() <= 1e-3
     dq_r, dk_r, dv_r = c.ref()
-    for sched in schedules(S, D, causal):
-        say(f"grouped parity {case} schedule={sched or 'atomic'}")
-        dq, dk, dv = c.run(sched)
-        assert tuple(dk.shape) == (B, Hkv, S, D) and tuple(dv.shape) == (B, Hkv, S, D)
-        for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
-            assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
+    try:
+        dab.set_dq_protocol(protocol)
+        for sched in schedules(S, D, causal):
+            say(f"grouped parity {case} schedule={sched or 'atomic'} dq protocol={protocol}")
+            dq, dk, dv = c.run(sched)
+            assert tuple(dk.shape) == (B, Hkv, S, D) and tuple(dv.shape) == (B, Hkv, S, D)
+            for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+                assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
+    finally:
+        dab.set_dq_protocol("auto")
 
 
 def test_grouped_bitwise_reproducible_20_runs():
