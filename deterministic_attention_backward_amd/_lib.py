@@ -43,6 +43,7 @@ EXPORTS = (
     "attn_probe_mfma",
     "attn_debug_wait_profile",
     "attn_debug_wait_timeouts",
+    "attn_debug_order_violations",
 )
 
 _lib = None
@@ -119,6 +120,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.attn_debug_wait_profile.restype = i
     lib.attn_debug_wait_timeouts.argtypes = [i]
     lib.attn_debug_wait_timeouts.restype = i
+    lib.attn_debug_order_violations.argtypes = [i]
+    lib.attn_debug_order_violations.restype = i
     return lib
 
 

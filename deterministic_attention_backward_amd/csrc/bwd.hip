@@ -200,6 +200,11 @@ __device__ __forceinline__ void lds_barrier() {
 #endif
 constexpr bool kProfileWait = ATTN_PROFILE_WAIT != 0;
 __device__ unsigned long long g_wait_prof[kMaxGrid][6];
+// Profiling build: dQ ordering checks. A wave that waits for its turn must
+// never see its flag beyond its rank (someone handed over out of order), and
+// a wave that hands over must find its flag still at its own rank (nobody
+// else advanced it). Violations are counted here (attn_debug_order_violations).
+__device__ unsigned g_order_violations;
 static int g_last_grid = 0;
 
 struct WaitClock {
@@ -675,7 +680,14 @@ struct DqRole {
   // contributor of the same blocks that it may go ahead.
   __device__ __forceinline__ void release() {
     if (!ATOMIC && pend >= 0) {
+      // (profiling build: the counter is read before the wait below, so its
+      // latency hides behind that of the stores)
+      int now = 0;
+      if constexpr (kProfileWait) now = XCD ? l2_load(&p.flags[pend]) : sys_load(&p.flags[pend]);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (kProfileWait) {
+        if (__builtin_amdgcn_readfirstlane(now) != pend_val - 1 && lane == 0) atomicAdd(&g_order_violations, 1u);
+      }
       if (lane == 0) {
         if (XCD) l2_store(&p.flags[pend], pend_val);
         else sys_store(&p.flags[pend], pend_val);
@@ -758,6 +770,12 @@ struct DqRole {
     int seen = flag_read(fl);
     uint32_t it = 0;
     while (seen != target) {
+      if constexpr (kProfileWait) {
+        if (seen > target) {  // handed over past this contributor's rank
+          if (lane == 0) atomicAdd(&g_order_violations, 1u);
+          break;
+        }
+      }
       if (++it >= p.wait_limit) {
         if (lane == 0) note_timeout(p.header);
         break;
@@ -1249,6 +1267,19 @@ extern "C" int attn_debug_wait_profile(uint64_t* out, int max_workgroups) {
   for (int g = 0; g < n; ++g)
     for (int k = 0; k < 6; ++k) out[6 * g + k] = rows[g][k];
   return n;
+}
+
+extern "C" int attn_debug_order_violations(int reset) {
+  if (!attn::kProfileWait) return ATTN_ERR_UNSUPPORTED;
+  if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
+  unsigned n = 0;
+  if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(attn::g_order_violations), sizeof(n)) != hipSuccess) return ATTN_ERR_HIP;
+  if (reset) {
+    const unsigned zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(attn::g_order_violations), &zero, sizeof(zero)) != hipSuccess)
+      return ATTN_ERR_HIP;
+  }
+  return n > 0x7fffffffu ? 0x7fffffff : (int)n;
 }
 
 extern "C" int attn_debug_wait_timeouts(int reset) {

@@ -254,6 +254,20 @@ int attn_probe_mfma(int iterations, void* stream, double* tflops, double* ghz);
  */
 int attn_debug_wait_profile(uint64_t* out, int max_workgroups);
 
+/*
+ * attn_debug_order_violations - only in the profiling build (as above); the
+ * regular build returns ATTN_ERR_UNSUPPORTED. In that build every dQ hand-off
+ * of the deterministic modes checks the ordered-reduction invariant of the
+ * DASH paper's dQ accumulation (section 3, the fixed per-tile order): a
+ * contributor of rank r that waits for its turn must never see the tile's
+ * counter beyond r, and when it hands over, the counter must still read r
+ * (no other contributor advanced it). Synchronises the device and returns how
+ * many checks failed since the count was last cleared, over every backward
+ * launch of this process (>= 0), or a negative status. reset != 0 clears the
+ * count after reading. Host-blocking; for tests.
+ */
+int attn_debug_order_violations(int reset);
+
 #ifdef __cplusplus
 }
 #endif

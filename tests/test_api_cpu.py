@@ -53,6 +53,11 @@ def test_tile_choice():
     assert lib.attn_bwd_tile(0, 64, 0) == _lib.ERR_INVALID_ARG
 
 
+def test_order_checks_only_in_profiling_build():
+    # the regular build carries no ordering checks and says so without touching a device
+    assert _lib.load().attn_debug_order_violations(0) == _lib.ERR_UNSUPPORTED
+
+
 def test_workspace_size():
     B, H, S, D = 4, 16, 2048, 128
     n = dab.workspace_size(B, H, S, D, False, "naive")

@@ -53,3 +53,34 @@ def test_profiling_build_is_bitwise_identical(causal, sched):
     rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
     assert sum(r[5] for r in rows) > 0            # sub-tiles were counted
     assert all(r[2] <= r[4] and r[0] <= r[1] for r in rows)  # waits are part of the total
+
+
+@pytest.mark.parametrize("protocol", ["xcd_local", "device"])
+def test_profiling_build_dq_order_checks_pass(protocol):
+    """Every dQ hand-off of every schedule keeps the fixed order: the profiling
+    build counts a contributor that finds its tile counter past its rank while
+    waiting, or moved by someone else before it hands over."""
+    prof = _lib.load_profile()
+    assert _lib.load().attn_debug_order_violations(0) == _lib.ERR_UNSUPPORTED
+    saved = _lib._lib
+    try:
+        _lib._lib = prof
+        dab.set_dq_protocol(protocol)
+        prof.attn_debug_order_violations(1)
+        prof.attn_debug_wait_timeouts(1)
+        cases = [(1, 4, 4, 1024, 128), (1, 4, 4, 1024, 64), (1, 8, 2, 1024, 128)]
+        for B, H, Hkv, S, D in cases:
+            for causal in (False, True):
+                x = attn_inputs.draw_grouped(B, H, Hkv, S, D, 73) if Hkv != H else attn_inputs.draw(B, H, S, D, 73)
+                q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+                o, lse = dab.fwd(q, k, v, causal)
+                for sched in ("naive", "descending", "shift") + (("symmetric_shift",) if causal else ()):
+                    print(f"order checks: {protocol} B={B} H={H} Hkv={Hkv} S={S} D={D} "
+                          f"causal={causal} {sched}", flush=True)
+                    dab.bwd(q, k, v, o, do, lse, causal, sched)
+                    torch.cuda.synchronize()
+                    assert prof.attn_debug_order_violations(1) == 0, (B, H, Hkv, S, D, causal, sched)
+        assert prof.attn_debug_wait_timeouts(1) == 0
+    finally:
+        dab.set_dq_protocol("auto")
+        _lib._lib = saved
