@@ -171,12 +171,15 @@ def wait_profile(w, sched, args, torch, dab, _lib, tensors):
         _lib._lib = prof
         dab.set_dq_protocol(args.dq_protocol)
         ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, sched, w.tile, Hkv=w.kv_heads)
+        prof.attn_debug_order_violations(1)
         for _ in range(2):
             dab.bwd(q, k, v, o, do, lse, w.causal, sched, w.scale, w.tile, ws)
         torch.cuda.synchronize()
         buf = (ctypes.c_uint64 * (6 * 1024))()
         n = prof.attn_debug_wait_profile(buf, 1024)
         _lib.check(min(n, 0), "attn_debug_wait_profile")
+        bad = prof.attn_debug_order_violations(1)
+        _lib.check(min(bad, 0), "attn_debug_order_violations")
     finally:
         _lib._lib = saved
     rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
@@ -186,6 +189,7 @@ def wait_profile(w, sched, args, torch, dab, _lib, tensors):
             "dq_waves_turn_wait_frac": round(tot[2] / max(tot[4], 1), 4),
             "dq_waves_barrier_frac": round(tot[3] / max(tot[4], 1), 4),
             "turn_wait_cycles_per_subtile": round(tot[2] / max(tot[5], 1), 1),
+            "dq_order_violations": bad,
             "note": "s_memtime cycles of one tile wave and one dQ wave per workgroup, profiling build"}
 
 
