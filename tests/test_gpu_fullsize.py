@@ -76,3 +76,65 @@ def test_fullsize_sampled_parity(name):
         assert torch.all(dk_sum.abs() <= 1e-2 * dk_scale + 1e-3), f"{name} {sched}: sum dK"
         assert torch.all((dv_sum - do_sum).abs() <= 1e-2 * do.float().abs().sum(dim=2) + 1e-3), f"{name} {sched}: sum dV"
         del ws
+
+
+def test_fullsize_grouped_sampled_parity():
+    """The grouped-query workload (32 query heads over 8 K/V heads, causal 4k,
+    D 128) at full size: sampled rows against the oracle, where a K/V head's
+    dK/dV rows are the sums of its query heads' rows, and the column sums per
+    K/V head (sum_j dK_j = 0, sum_j dV_j = sum over its query heads of
+    sum_i dO_i). Per element the grouped tolerance |x - ref| <= 2e-2 +
+    2^-8 |ref| applies, since a K/V head's gradients sum G query heads'
+    contributions and round to bf16 at their own size."""
+    w = attn_inputs.WORKLOADS["C3G"]
+    G = w.H // w.kv_heads
+    T = dab.tile(w.S, w.D, w.tile)
+    N = -(-w.S // T)
+    x = attn_inputs.draw_workload(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    assert k.shape[1] == w.kv_heads
+    o, lse = dab.fwd(q, k, v, w.causal, w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.S, T)
+    f64 = lambda t: t.float().cpu().double().numpy()
+    refs = {}
+    for b, kvh in [(0, 0), (w.B - 1, w.kv_heads - 1)]:
+        kk, vv = f64(k[b, kvh]), f64(v[b, kvh])
+        dq_rows, dk_sum, dv_sum = {}, 0.0, 0.0
+        for h in range(kvh * G, (kvh + 1) * G):
+            assert A.group_of(w.H, w.kv_heads, h) == kvh
+            rq, rk, rv = A.backward_rows_head(f64(q[b, h]), kk, vv, f64(o[b, h]), f64(do[b, h]), f64(lse[b, h]),
+                                              w.causal, w.scale, rows, rows)
+            dq_rows[h] = rq
+            dk_sum = dk_sum + rk
+            dv_sum = dv_sum + rv
+        refs[(b, kvh)] = (dq_rows, dk_sum, dv_sum)
+
+    def close(label, got, ref):
+        mx, rel = A.compare(got, ref)
+        excess = float(np.max(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)))
+        assert excess <= 2e-2 and rel <= 5e-3, f"C3G {label}: {mx:.3e} beyond rounding {excess:.3e} rel {rel:.3e}"
+
+    do_group = do.float().sum(dim=2).view(w.B, w.kv_heads, G, w.D).sum(dim=2)
+    do_scale = do.float().abs().sum(dim=2).view(w.B, w.kv_heads, G, w.D).sum(dim=2)
+    for sched in schedules(w, N):
+        say(f"full-size C3G {w.describe()} T={T} schedule={sched or 'atomic'}")
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, sched or "naive", w.tile, Hkv=w.kv_heads)
+        if sched is None:
+            dq, dk, dv = dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws)
+        else:
+            dq, dk, dv = dab.bwd(q, k, v, o, do, lse, w.causal, sched, w.scale, w.tile, ws)
+            dab.check_workspace(ws)
+        torch.cuda.synchronize()
+        assert tuple(dk.shape) == (w.B, w.kv_heads, w.S, w.D)
+        for (b, kvh), (dq_rows, rk, rv) in refs.items():
+            tag = f"{sched or 'atomic'} head {(b, kvh)}"
+            for h, rq in dq_rows.items():
+                close(f"{tag} dQ of query head {h}", f64(dq[b, h, rows]), rq)
+            close(f"{tag} dK", f64(dk[b, kvh, rows]), rk)
+            close(f"{tag} dV", f64(dv[b, kvh, rows]), rv)
+        dk_sum = dk.float().sum(dim=2)
+        dv_sum = dv.float().sum(dim=2)
+        assert torch.all(dk_sum.abs() <= 1e-2 * dk.float().abs().sum(dim=2) + 1e-3), f"C3G {sched}: sum dK"
+        assert torch.all((dv_sum - do_group).abs() <= 1e-2 * do_scale + 1e-3), f"C3G {sched}: sum dV"
+        del ws
