@@ -424,7 +424,10 @@ struct TileRole {
     }
   }
 
-  // P = exp2(S scale log2(e) - LSE log2(e)) and dS = P (dP - Delta), in place
+  // P = exp2(S scale log2(e) - LSE log2(e)) and dS = P (dP - Delta), in place.
+  // The exponent is one explicit fused multiply-add, so its rounding (and with
+  // it every bit downstream) does not depend on how the compiler schedules
+  // this code.
   __device__ __forceinline__ void soft(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
                                        f32x16& dp) {
     const float* Ls = L.lse(buf);
@@ -440,7 +443,7 @@ struct TileRole {
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * g + b;
           const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
-          float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+          float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
           const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
           pv = vis ? pv : 0.0f;
           s[i] = pv;
@@ -455,7 +458,7 @@ struct TileRole {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * g + b;
-          const float pv = fast_exp2(s[i] * p.scale_log2 - L4[b]);
+          const float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
           s[i] = pv;
           dp[i] = pv * (dp[i] - D4[b]);
         }
