@@ -68,7 +68,7 @@ def test_profiling_build_dq_order_checks_pass(protocol):
         dab.set_dq_protocol(protocol)
         prof.attn_debug_order_violations(1)
         prof.attn_debug_wait_timeouts(1)
-        cases = [(1, 4, 4, 1024, 128), (1, 4, 4, 1024, 64), (1, 8, 2, 1024, 128)]
+        cases = [(1, 4, 4, 1024, 128), (1, 4, 4, 1024, 64), (1, 8, 2, 1024, 128), (1, 16, 16, 4096, 128)]
         for B, H, Hkv, S, D in cases:
             for causal in (False, True):
                 x = attn_inputs.draw_grouped(B, H, Hkv, S, D, 73) if Hkv != H else attn_inputs.draw(B, H, S, D, 73)
