@@ -158,6 +158,33 @@ def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
     }
 
 
+def host_info(torch):
+    """CPU model, host threads and the ROCm/HIP build the run used."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_threads": os.cpu_count(), "hip": getattr(torch.version, "hip", None),
+            "torch": torch.__version__, "gpu": torch.cuda.get_device_name(0)}
+
+
+def repeat_check(fn, runs, torch):
+    """Untimed: run a deterministic call `runs` times and count the runs whose
+    dQ, dK and dV carry the first run's bits."""
+    ref = [t.clone() for t in fn()]
+    same = 1
+    for _ in range(runs - 1):
+        got = fn()
+        torch.cuda.synchronize()
+        same += all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, got))
+    return same
+
+
 def rnd(x):
     return {k: round(v, 4) for k, v in x.items()} if isinstance(x, dict) else round(x, 4)
 
@@ -346,6 +373,10 @@ def main():
                 "probe": "one workgroup per CU, 4 waves, 4 independent bf16 32x32x16 MFMA chains per wave"}
         log(f"measured dense bf16 MFMA peak {tf.value:.1f} TFLOP/s at {ghz.value:.3f} GHz (s_memtime rate)")
     best = min(results, key=lambda s: results[s]["ms"])
+    ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, best, w.tile, Hkv=w.kv_heads)
+    same = repeat_check(lambda: dab.bwd(q, k, v, o, do, lse, w.causal, best, w.scale, w.tile, ws, out), 20, torch)
+    del ws
+    log(f"repeatability ({best}, untimed): {same} of 20 runs give the first run's bits")
     wait = None
     if args.wait_profile:
         wait = wait_profile(w, best, args, torch, dab, _lib, (q, k, v, o, do, lse))
@@ -374,6 +405,7 @@ def main():
                           "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"]),
                           "wait_timeouts": v["wait_timeouts"]} for s, v in results.items()},
         "dq_wait_timeouts": sum(v["wait_timeouts"] for v in results.values()),
+        "bitwise_identical_runs": {"schedule": best, "runs": 20, "identical": same},
         "nondet": {k2: rnd(v2) for k2, v2 in nondet.items()} if nondet else None,
         "mfma_measured": mfma,
         "pct_measured_mfma_peak": round(100.0 * r["tflops"] / mfma["tflops"], 2) if mfma else None,
@@ -385,6 +417,7 @@ def main():
     }
     if wait is not None:
         line["wait_profile"] = wait
+    line["host"] = host_info(torch)
     if args.cpu_seconds > 0:
         x_cpu = {n: x[n] for n in ("q", "k", "v", "do")}
         line["cpu_baseline"] = cpu_baseline(w, x_cpu, o.cpu(), lse.cpu(), args.cpu_seconds)
