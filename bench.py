@@ -169,8 +169,9 @@ def host_info(torch):
                     break
     except OSError:
         pass
+    gpu = torch.cuda.get_device_name(0) if torch.cuda.is_available() else None
     return {"cpu_model": model, "cpu_threads": os.cpu_count(), "hip": getattr(torch.version, "hip", None),
-            "torch": torch.__version__, "gpu": torch.cuda.get_device_name(0)}
+            "torch": torch.__version__, "gpu": gpu}
 
 
 def repeat_check(fn, runs, torch):
@@ -180,7 +181,8 @@ def repeat_check(fn, runs, torch):
     same = 1
     for _ in range(runs - 1):
         got = fn()
-        torch.cuda.synchronize()
+        if torch.cuda.is_available():
+            torch.cuda.synchronize()
         same += all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref, got))
     return same
 
