@@ -219,3 +219,37 @@ def test_workspace_reuse_sees_fresh_accumulators(sched):
         for name, a, b in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
             err = (a.float() - b.float()).abs().max().item()
             assert err <= 2e-2, f"{sched} seed {seed} {name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("case", [(1, 3, 300, 128, True, 81), (2, 2, 256, 64, False, 82)],
+                         ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "f"))
+def test_parity_with_a_caller_softmax_scale(case):
+    """A softmax scale other than 1/sqrt(D) reaches every step: the forward's
+    scores and LSE, the backward's P (through scale log2 e) and dK's factor.
+    The scale is 0.6 / sqrt(D), below the default, so the gradients are no
+    larger than at the default scale and the target's tolerance applies as
+    it stands (a kernel that used the default scale instead would miss by
+    far more)."""
+    B, H, S, D, causal, seed = case
+    scale = 0.6 / math.sqrt(D)
+    say(f"caller scale {scale:.4f}: B={B} H={H} S={S} D={D} causal={causal}")
+    x = attn_inputs.draw(B, H, S, D, seed)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = dab.fwd(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    nq, nk, nv, ndo, no, nlse = (f64(t) for t in (q, k, v, do, o, lse))
+    o_ref, lse_ref = A.forward(nq, nk, nv, causal, scale)
+    assert_close("O", no, o_ref)
+    assert np.abs(nlse - lse_ref).max() <= 1e-3
+    dq_r, dk_r, dv_r = A.backward(nq, nk, nv, no, ndo, nlse, causal, scale)
+    N = -(-S // dab.tile(S, D))
+    scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if causal and N % 2 == 0 else [])
+    for sched in scheds + [None]:
+        say(f"caller scale {scale:.4f}: schedule={sched or 'atomic'}")
+        if sched is None:
+            dq, dk, dv = dab.bwd_nondeterministic(q, k, v, o, do, lse, causal, scale)
+        else:
+            dq, dk, dv = dab.bwd(q, k, v, o, do, lse, causal, sched, scale)
+        torch.cuda.synchronize()
+        for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
+            assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
