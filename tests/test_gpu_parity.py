@@ -253,3 +253,29 @@ def test_parity_with_a_caller_softmax_scale(case):
         torch.cuda.synchronize()
         for name, g, r in (("dQ", dq, dq_r), ("dK", dk, dk_r), ("dV", dv, dv_r)):
             assert_close(f"{sched or 'atomic'} {name}", f64(g), r)
+
+
+def test_calls_run_on_the_callers_stream():
+    """Forward and backward issued under a side stream (default priority)
+    give the default stream's bits: every launch and the workspace set-up go
+    to the caller's stream, in order."""
+    B, H, S, D = 2, 4, 640, 128
+    say(f"side stream: B={B} H={H} S={S} D={D}")
+    x = attn_inputs.draw(B, H, S, D, 91)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = dab.fwd(q, k, v, True)
+    ref = dab.bwd(q, k, v, o, do, lse, True, "shift")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o2, lse2 = dab.fwd(q, k, v, True)
+        got = dab.bwd(q, k, v, o2, do, lse2, True, "shift")
+        nondet = dab.bwd_nondeterministic(q, k, v, o2, do, lse2, True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for a, b in zip(ref, nondet):
+        assert (a.float() - b.float()).abs().max().item() <= 2e-2
