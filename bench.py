@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the deterministic attention backward on one MI355X.
 
-One step = one call of the deterministic backward (pre-pass + main tile
-kernel with the ordered dQ reduction; the last contributor writes dq), on
-synthetic bf16 inputs already resident in HBM. The default workload is the
-full-mask B=4, H=16, S=2048, D=128 case. Every deterministic schedule valid
-for the mask is timed, then the atomic-dQ variant; `value` is the fastest
-deterministic schedule's throughput under the FLOP convention
-2.5 * 4 * B * H * S^2 * D (halved for a causal mask).
+One step = one call of the deterministic backward (pre-pass, main tile
+kernel with the ordered dQ reduction, and the post-pass that converts the
+fp32 dQ accumulator to bf16 dq), on synthetic bf16 inputs already resident
+in HBM. The headline workload is the causal B=4, H=32, S=4096, D=128 case;
+the same shape with a full mask is measured in the same run and carried as
+a sub-record of the line. Every deterministic schedule valid for the mask is
+timed, then the atomic-dQ variant; `value` is the fastest deterministic
+schedule's throughput under the FLOP convention 2.5 * 4 * B * H * S^2 * D
+(halved for a causal mask).
 
 Printed (one JSON line on stdout): the metric, value (TFLOP/s), % of the bf16
 dense MFMA peak, the deterministic/non-deterministic ratio, per-schedule
@@ -15,7 +17,7 @@ numbers, the roofline of the main tile kernel (its duration taken with HIP
 events recorded around its launch on its own stream) and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3] [--also C3F]
 """
 
 from __future__ import annotations
@@ -104,13 +106,13 @@ KERNEL_SOURCES = ("bwd.hip", "common.hpp", "lds.hpp", "schedule.hpp", "launch.hp
 def measured_traffic(workload: str, schedule: str, protocol: str):
     """HBM bytes per launch of the main kernel from the committed counter record.
 
-    profiles/bwd_main_C2_traffic.json holds FETCH_SIZE + WRITE_SIZE (scaled by
-    a 1 GiB copy) for one workload/schedule, with a hash of the kernel sources it
-    was taken on. Returns None unless it matches this run and the sources are
-    unchanged since.
+    profiles/bwd_main_<workload>_traffic.json holds FETCH_SIZE + WRITE_SIZE
+    (scaled by a 1 GiB copy) for one workload/schedule, with a hash of the
+    kernel sources it was taken on. Returns None unless it matches this run and
+    the sources are unchanged since.
     """
     import hashlib
-    path = os.path.join(ROOT, "profiles", "bwd_main_C2_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"bwd_main_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -283,12 +285,80 @@ def block_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def measure(w, args, torch, dab, _lib, lib, events):
+    """Time every deterministic schedule valid for the workload's mask and the
+    atomic-dQ variant on one synthetic draw; returns a record of the results
+    plus the inputs (for the CPU baseline and the profiles)."""
+    import attn_inputs
+    log(f"workload {w.name}: {w.describe()} seed={w.seed}")
+    x = attn_inputs.draw_workload(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = dab.fwd(q, k, v, w.causal, w.scale)
+    torch.cuda.synchronize()
+    T = dab.tile(w.S, w.D, w.tile)
+    N = -(-w.S // T)
+    if args.schedules:
+        scheds = args.schedules.split(",")
+    else:
+        scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else [])
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    results = {}
+    dab.wait_timeouts(reset=True)
+    for s in scheds:
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile, Hkv=w.kv_heads)
+        fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
+        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        dab.check_workspace(ws)
+        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api,
+                      "wait_timeouts": dab.wait_timeouts(reset=True)}
+        log(f"  {s:16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {results[s]['tflops']:7.1f} TFLOP/s")
+        if results[s]["wait_timeouts"]:
+            log(f"  WARNING: {results[s]['wait_timeouts']} bounded dQ waits ran out during the {s} calls")
+        del ws
+    nondet = None
+    if not args.no_nondet:
+        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile, Hkv=w.kv_heads)
+        fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
+        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
+        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
+        log(f"  {'atomic (non-det)':16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {nondet['tflops']:7.1f} TFLOP/s")
+        del ws
+    best = min(results, key=lambda s: results[s]["ms"])
+    ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, best, w.tile, Hkv=w.kv_heads)
+    same = repeat_check(lambda: dab.bwd(q, k, v, o, do, lse, w.causal, best, w.scale, w.tile, ws, out), 20, torch)
+    del ws
+    log(f"repeatability ({best}, untimed): {same} of 20 runs give the first run's bits")
+    r = results[best]
+    achieved = w.flops / (r["kernel_ms"] * 1e-3) / 1e12
+    rec = {
+        "workload": f"{w.name}: {w.describe()}", "schedule": best, "tile": T, "n_tiles": N, "seed": w.seed,
+        "flops_per_step": w.flops,
+        "value": round(r["tflops"], 2), "ms_per_step": round(r["ms"], 4),
+        "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,
+        "schedules": {s: {"ms": round(v["ms"], 4), "kernel_ms": round(v["kernel_ms"], 4),
+                          "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"]),
+                          "wait_timeouts": v["wait_timeouts"]} for s, v in results.items()},
+        "dq_wait_timeouts": sum(v["wait_timeouts"] for v in results.values()),
+        "bitwise_identical_runs": {"schedule": best, "runs": 20, "identical": same},
+        "nondet": {k2: rnd(v2) for k2, v2 in nondet.items()} if nondet else None,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, best, args.dq_protocol),
+                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
+                     "kernel": "bwd_main_kernel", "kernel_ms": round(r["kernel_ms"], 4)},
+    }
+    return rec, (x, q, k, v, o, do, lse)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--workload", default="C3", help="headline workload (default: causal 4k, D 128)")
+    ap.add_argument("--also", default="C3F",
+                    help="comma list of workloads measured in the same run as sub-records ('' = none)")
     ap.add_argument("--schedules", default="", help="comma list; default: every schedule valid for the mask")
     ap.add_argument("--no-nondet", action="store_true")
     ap.add_argument("--dq-protocol", default="auto", choices=["auto", "device", "xcd_local"],
@@ -322,40 +392,10 @@ def main():
     dab.set_dq_protocol(args.dq_protocol)
     events = HipEvents()
     w = attn_inputs.WORKLOADS[args.workload]
-    log(f"workload {w.name}: {w.describe()} seed={w.seed}")
-    x = attn_inputs.draw_workload(w)
-    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
-    o, lse = dab.fwd(q, k, v, w.causal, w.scale)
-    torch.cuda.synchronize()
-    T = dab.tile(w.S, w.D, w.tile)
-    N = -(-w.S // T)
-
-    if args.schedules:
-        scheds = args.schedules.split(",")
-    else:
-        scheds = ["naive", "descending", "shift"] + (["symmetric_shift"] if w.causal and N % 2 == 0 else [])
-    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    results = {}
-    dab.wait_timeouts(reset=True)
-    for s in scheds:
-        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, s, w.tile, Hkv=w.kv_heads)
-        fn = lambda s=s, ws=ws: dab.bwd(q, k, v, o, do, lse, w.causal, s, w.scale, w.tile, ws, out)
-        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
-        dab.check_workspace(ws)
-        results[s] = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api,
-                      "wait_timeouts": dab.wait_timeouts(reset=True)}
-        log(f"  {s:16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {results[s]['tflops']:7.1f} TFLOP/s")
-        if results[s]["wait_timeouts"]:
-            log(f"  WARNING: {results[s]['wait_timeouts']} bounded dQ waits ran out during the {s} calls")
-        del ws
-    nondet = None
-    if not args.no_nondet:
-        ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile, Hkv=w.kv_heads)
-        fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
-        ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
-        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
-        log(f"  {'atomic (non-det)':16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {nondet['tflops']:7.1f} TFLOP/s")
-        del ws
+    head, (x, q, k, v, o, do, lse) = measure(w, args, torch, dab, _lib, lib, events)
+    subs = {}
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        subs[name], _ = measure(attn_inputs.WORKLOADS[name], args, torch, dab, _lib, lib, events)
 
     if args.copy_calibration:
         nbytes = 1 << 30
@@ -374,49 +414,35 @@ def main():
         mfma = {"tflops": round(tf.value, 1), "sclk_ghz": round(ghz.value, 3),
                 "probe": "one workgroup per CU, 4 waves, 4 independent bf16 32x32x16 MFMA chains per wave"}
         log(f"measured dense bf16 MFMA peak {tf.value:.1f} TFLOP/s at {ghz.value:.3f} GHz (s_memtime rate)")
-    best = min(results, key=lambda s: results[s]["ms"])
-    ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, best, w.tile, Hkv=w.kv_heads)
-    same = repeat_check(lambda: dab.bwd(q, k, v, o, do, lse, w.causal, best, w.scale, w.tile, ws, out), 20, torch)
-    del ws
-    log(f"repeatability ({best}, untimed): {same} of 20 runs give the first run's bits")
     wait = None
     if args.wait_profile:
-        wait = wait_profile(w, best, args, torch, dab, _lib, (q, k, v, o, do, lse))
-        log(f"wait profile ({best}): {wait}")
-    r = results[best]
-    achieved = w.flops / (r["kernel_ms"] * 1e-3) / 1e12
+        wait = wait_profile(w, head["schedule"], args, torch, dab, _lib, (q, k, v, o, do, lse))
+        log(f"wait profile ({head['schedule']}): {wait}")
     line = {
         "metric": METRIC,
-        "value": round(r["tflops"], 2),
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.describe()}", "schedule": best, "tile": T, "n_tiles": N,
-                   "dq_protocol": args.dq_protocol,
-                   "seed": w.seed, "flops_per_step": w.flops},
-        "pct_mfma_peak": round(100.0 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
-        "ratio_vs_nondet": round(nondet["ms"] / r["ms"], 4) if nondet else None,
-        "schedules": {s: {"ms": round(v["ms"], 4), "kernel_ms": round(v["kernel_ms"], 4),
-                          "tflops": round(v["tflops"], 2), "api_ms": rnd(v["api_ms"]),
-                          "wait_timeouts": v["wait_timeouts"]} for s, v in results.items()},
-        "dq_wait_timeouts": sum(v["wait_timeouts"] for v in results.values()),
-        "bitwise_identical_runs": {"schedule": best, "runs": 20, "identical": same},
-        "nondet": {k2: rnd(v2) for k2, v2 in nondet.items()} if nondet else None,
-        "mfma_measured": mfma,
-        "pct_measured_mfma_peak": round(100.0 * r["tflops"] / mfma["tflops"], 2) if mfma else None,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, best, args.dq_protocol),
-                     "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE)",
-                     "kernel": "bwd_main_kernel", "kernel_ms": round(r["kernel_ms"], 4)},
+        "config": {"workload": head["workload"], "schedule": head["schedule"], "tile": head["tile"],
+                   "n_tiles": head["n_tiles"], "dq_protocol": args.dq_protocol, "seed": head["seed"],
+                   "flops_per_step": head["flops_per_step"]},
+        "pct_mfma_peak": head["pct_mfma_peak"],
+        "ratio_vs_nondet": head["ratio_vs_nondet"],
     }
+    for key in ("schedules", "dq_wait_timeouts", "bitwise_identical_runs", "nondet"):
+        line[key] = head[key]
+    line["mfma_measured"] = mfma
+    line["pct_measured_mfma_peak"] = round(100.0 * head["value"] / mfma["tflops"], 2) if mfma else None
+    line["roofline"] = head["roofline"]
+    line["sub_records"] = subs
     if wait is not None:
         line["wait_profile"] = wait
     line["host"] = host_info(torch)

@@ -56,6 +56,7 @@ __device__ __forceinline__ int ctl_read(int* w) {
 
 // Number of bounded waits that ran out since the last read (all launches of
 // this process on this device); read and cleared by attn_debug_wait_timeouts.
+// header[1] marks the call itself as failed: its post-passes write NaN outputs.
 __device__ int g_wait_timeouts;
 
 __device__ __forceinline__ void note_timeout(int* header) {
@@ -311,9 +312,9 @@ struct TileRole {
   Lds<G> L;
   int tid, lane, a, l32, hh;
   // staged-row addressing (see swz): row-wise reads of row l32, chunk 2c + hh at
-  // a_base + 32 (c ^ sw1); transposed reads, 4 rows from 4 hh + e, features
-  // from 32 n + 16 (group & 1) + 4 t, at tr_base[part] + 64 (n ^ thi)
-  int a_base, sw1, tr_base[2], thi;
+  // a_base + 32 (c ^ sw1); transposed reads (TrLane) at tl.base[part] + 64 (n ^ tl.hi)
+  int a_base, sw1;
+  TrLane tl;
   static constexpr bool VL = G::V_LDS;
   bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
@@ -329,11 +330,7 @@ struct TileRole {
     const int sw = swz<G::D>(l32);
     a_base = l32 * G::RB + 16 * ((hh ^ sw) & 1);
     sw1 = sw >> 1;
-    const int g = lane >> 4, e = (lane >> 2) & 3, t = lane & 3;
-    thi = G::D == 128 ? e : e >> 1;
-#pragma unroll
-    for (int part = 0; part < 2; ++part)
-      tr_base[part] = (4 * hh + e) * G::RB + 16 * ((2 * (g & 1) + (t >> 1)) ^ (2 * part + hh)) + 8 * (t & 1);
+    tl.init<G::D>(lane);
   }
 
   __device__ __forceinline__ void park(const Seg& sg, bool load) {
@@ -466,13 +463,9 @@ struct TileRole {
     }
   }
 
-  // dS^T of row block m to LDS; dV += P^T dO and dK += dS^T Q
-  // B operand of feature block n, query half h2 of row block m: 8 queries in
-  // the order of the C-matrix rows the lane holds (4 hh + 0..3, 8 + 4 hh + 0..3)
-  __device__ __forceinline__ static bf16x8 trB(const char* blk, int h2, const int* tb, int nx) {
-    return cat44(lds_read_tr((const bf16*)(blk + 16 * h2 * G::RB + tb[0] + nx)),
-                 lds_read_tr((const bf16*)(blk + (16 * h2 + 8) * G::RB + tb[1] + nx)));
-  }
+  // dS^T of row block m to LDS; dV += P^T dO and dK += dS^T Q. B operand of
+  // feature block n, query half h2 of row block m (trB): 8 queries in the
+  // order of the C-matrix rows the lane holds (4 hh + 0..3, 8 + 4 hh + 0..3)
 
   __device__ __forceinline__ void accumulate(int m, int buf) {
     accumulate(m, buf, pack8(s, 0), pack8(s, 8), pack8(dp, 0), pack8(dp, 8));
@@ -483,26 +476,26 @@ struct TileRole {
     *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
     *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
     *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
-    int tb[2] = {tr_base[0], tr_base[1]}, th = thi;
+    int tb[2] = {tl.base[0], tl.base[1]}, th = tl.hi;
     asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
     const char* QB = L.q(buf) + 32 * m * G::RB;
     const char* OB = L.o(buf) + 32 * m * G::RB;
     bf16x8 ov[2][2], qv[2][2];  // B operands one feature block ahead
     {
       const int nx = th << 6;
-      ov[0][0] = trB(OB, 0, tb, nx);
-      ov[0][1] = trB(OB, 1, tb, nx);
-      qv[0][0] = trB(QB, 0, tb, nx);
-      qv[0][1] = trB(QB, 1, tb, nx);
+      ov[0][0] = trB<G::RB>(OB, 0, tb, nx);
+      ov[0][1] = trB<G::RB>(OB, 1, tb, nx);
+      qv[0][0] = trB<G::RB>(QB, 0, tb, nx);
+      qv[0][1] = trB<G::RB>(QB, 1, tb, nx);
     }
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
       if (n + 1 < ND) {
         const int nx = ((n + 1) ^ th) << 6;
-        ov[(n + 1) & 1][0] = trB(OB, 0, tb, nx);
-        ov[(n + 1) & 1][1] = trB(OB, 1, tb, nx);
-        qv[(n + 1) & 1][0] = trB(QB, 0, tb, nx);
-        qv[(n + 1) & 1][1] = trB(QB, 1, tb, nx);
+        ov[(n + 1) & 1][0] = trB<G::RB>(OB, 0, tb, nx);
+        ov[(n + 1) & 1][1] = trB<G::RB>(OB, 1, tb, nx);
+        qv[(n + 1) & 1][0] = trB<G::RB>(QB, 0, tb, nx);
+        qv[(n + 1) & 1][1] = trB<G::RB>(QB, 1, tb, nx);
       }
       dVa[n] = mfma32(pb0, ov[n & 1][0], dVa[n]);
       dVa[n] = mfma32(pb1, ov[n & 1][1], dVa[n]);
@@ -1041,17 +1034,40 @@ __global__ void __launch_bounds__(T / 16 * 64) bwd_main_kernel(MainParams p) {
 // --------------------------------------------------------------------------------------
 // post-pass: dq = bf16(scale * dQ accumulator)
 
+// A tripped wait bound (header[1], set by the main kernel) makes the call's
+// results unusable: the dQ order may have been broken. The passes after the
+// main kernel then write NaN into every output instead of values, so the
+// failure shows in the gradients themselves, with no host synchronisation.
+__device__ __forceinline__ bool call_failed(const int* header) {
+  return __hip_atomic_load(&header[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+
+__device__ __forceinline__ void fill_nan(bf16* x, long long n, long long t0, long long nthreads) {
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(bf16, (unsigned short)0x7FC0);
+  for (long long i = t0; i < n / 8; i += nthreads) *(bf16x8*)(x + 8 * i) = v;
+}
+
 template <int D>
-__global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, long long BH, int S,
-                                                       int S_pad, int BR, int quad_major, float scale) {
+__global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, bf16* dk, bf16* dv,
+                                                       const int* header, long long BH, int S, int S_pad, int BR,
+                                                       int quad_major, float scale, long long kv_elems) {
   // dq_ws holds, per query sub-tile of BR rows, 32 x 32 blocks in MFMA register
   // order (see the dQ waves: quad-major or element-major within a block); one
   // thread converts accumulators 4g..4g+3 of one lane: four consecutive rows
   // of one feature column.
   constexpr int ND = D / 32;
+  const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long nthreads = (long long)gridDim.x * blockDim.x;
+  if (call_failed(header)) {
+    fill_nan(dq, BH * S * D, t0, nthreads);
+    fill_nan(dk, kv_elems, t0, nthreads);
+    fill_nan(dv, kv_elems, t0, nthreads);
+    return;
+  }
   const long long n4 = BH * S_pad * (D / 4);
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (long long)gridDim.x * blockDim.x) {
+  for (long long i = t0; i < n4; i += nthreads) {
     const long long sub = i / (BR * D / 4);  // bh * (S_pad / BR) + sub-tile
     const int r = (int)(i % (BR * D / 4));
     const int blk = r >> 8, g = (r >> 6) & 3, lane = r & 63;
@@ -1080,13 +1096,19 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
 // grouped-query epilogue: dK, dV of K/V head hk = the sum over its G query heads
 // hk G, ..., hk G + G - 1, added in that order (a fixed order: deterministic)
 
-__global__ void __launch_bounds__(256) bwd_gqa_reduce_kernel(const float* dkv, bf16* dk, bf16* dv, int H, int Hkv,
-                                                             int S, int S_pad, int D, long long BH) {
+__global__ void __launch_bounds__(256) bwd_gqa_reduce_kernel(const float* dkv, bf16* dk, bf16* dv, const int* header,
+                                                             int H, int Hkv, int S, int S_pad, int D, long long BH) {
   const int G = H / Hkv;
   const long long quads = (long long)(BH / H) * Hkv * S * (D / 4);  // output elements / 4
   const long long part = BH * S_pad * D;                             // floats per tensor of dkv
   const long long nthreads = (long long)gridDim.x * blockDim.x;
-  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < quads; t += nthreads) {
+  const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (call_failed(header)) {  // the post-pass has written NaN into dq; dk and dv follow
+    fill_nan(dk, quads * 4, t0, nthreads);
+    fill_nan(dv, quads * 4, t0, nthreads);
+    return;
+  }
+  for (long long t = t0; t < quads; t += nthreads) {
     const long long e = t * 4;                   // output element: ((b Hkv + hk) S + s) D + d
     const long long row = e / D;                 // (b Hkv + hk) S + s
     const int d = (int)(e - row * D);
@@ -1240,19 +1262,22 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   {
     const long long want = (BH * a.S_pad * (a.D / 4) + 255) / 256;
     const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+    // (grouped heads: dk and dv are written by the group sum below, which checks the flag itself)
+    const long long kv_elems = mp.group > 1 ? 0 : BH * a.S * a.D;
     if (a.D == 64)
-      hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.BR, atomic ? 0 : 1, a.scale);
+      hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, a.BR, atomic ? 0 : 1, a.scale, kv_elems);
     else
-      hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, BH, a.S,
-                         a.S_pad, a.BR, atomic ? 0 : 1, a.scale);
+      hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, a.BR, atomic ? 0 : 1, a.scale,
+                         kv_elems);
     e = hipGetLastError();
   }
   if (e == hipSuccess && mp.group > 1) {
     const long long want = ((long long)a.B * a.Hkv * a.S * (a.D / 4) + 255) / 256;
     const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
     hipLaunchKernelGGL(bwd_gqa_reduce_kernel, dim3(g), dim3(256), 0, stream, (const float*)mp.dkv, (bf16*)a.dk,
-                       (bf16*)a.dv, a.H, a.Hkv, a.S, a.S_pad, a.D, BH);
+                       (bf16*)a.dv, (const int*)header, a.H, a.Hkv, a.S, a.S_pad, a.D, BH);
     e = hipGetLastError();
   }
   return e;

@@ -133,7 +133,10 @@ int attn_bwd_nondeterministic(const void* q, const void* k, const void* v, const
 /*
  * attn_bwd_check - wait for `stream`, then report whether a deterministic call
  * that used `workspace` tripped the bound on a dQ ordering wait
- * (ATTN_ERR_TIMEOUT), else ATTN_OK. Host-blocking.
+ * (ATTN_ERR_TIMEOUT), else ATTN_OK. Host-blocking. A call that tripped the
+ * bound also writes NaN into every element of its dq, dk and dv (the passes
+ * after the main kernel read the workspace's flag), so the failure shows in
+ * the gradients without this check or any other host synchronisation.
  */
 int attn_bwd_check(const void* workspace, size_t workspace_bytes, void* stream);
 
@@ -185,10 +188,12 @@ int attn_schedule_plan(int n_tiles, int mask, int schedule, int32_t* out, size_t
  * hand-off flag read plus a short sleep) on a single dQ ordering wait; 0
  * restores the default (2^21, a few seconds at most). When a wait reaches the bound the
  * workgroup records ATTN_ERR_TIMEOUT in the workspace, stops waiting and
- * finishes normally; attn_bwd_check reports it. poison_counter != 0 makes the
+ * finishes normally; the call's outputs are then NaN and attn_bwd_check
+ * reports the status. poison_counter != 0 makes the
  * next deterministic calls wait on one dQ hand-off flag for a value it never
  * takes, so that the bound is certain to trip (used to test the timeout
- * path). Process-wide, not thread-safe; for tests only.
+ * path; that call's dq, dk and dv come out as NaN). Process-wide, not
+ * thread-safe; for tests only.
  */
 void attn_debug_set_wait_limit(uint32_t iterations, int poison_counter);
 

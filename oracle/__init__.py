@@ -16,8 +16,10 @@ Contents:
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things the
 oracle does not compute itself: finite differences, closed forms, invariants,
-torch's float64 autograd and ``scaled_dot_product_attention``, and brute force
-over tiny cases. No function here is "parity unpinned".
+torch's float64 autograd and ``scaled_dot_product_attention``, brute force
+over tiny cases, and hand-worked inputs (including ones that must be
+rejected) for the checkers ``attention.compare``, ``schedule.coverage_ok``,
+``schedule.chains_ok`` and ``schedule.conflict_free``.
 """
 
 from . import attention, schedule  # noqa: F401

@@ -249,12 +249,3 @@ def lemma1_edges(plan: Plan, c: float = 1.0, r: float = 1.0):
             if finish[("R", i, a)] > start[("R", i, b)]:
                 bad.append((i, a, b))
     return bad
-
-
-def head_plan_table(plan: Plan):
-    """Flat int list: [n_workers, n_tasks, then (worker, step, q, kv, rank) per task]."""
-    recs = plan.records()
-    flat = [len(plan.workers), len(recs)]
-    for rec in recs:
-        flat.extend(rec)
-    return flat

@@ -68,7 +68,11 @@ def test_autograd_gradients_meet_the_oracle():
     for name, got, ref in (("dQ", q.grad, dq_r), ("dK", k.grad, dk_r), ("dV", v.grad, dv_r)):
         g = f64(got)
         mx, rel = A.compare(g, ref)
-        excess = float(np.max(np.abs(g - ref) - 2.0 ** -8 * np.abs(ref)))
+        # dK and dV of a shared K/V head sum G query heads' shares and round to bf16
+        # at that size: their per-element bound widens by the output's rounding;
+        # dQ is per query head and keeps the plain bound
+        widen = 0.0 if name == "dQ" else 2.0 ** -8
+        excess = float(np.max(np.abs(g - ref) - widen * np.abs(ref)))
         assert excess <= 2e-2 and rel <= 5e-3, f"{name}: max_abs={mx:.3e} rel_l2={rel:.3e}"
 
 

@@ -154,3 +154,25 @@ def test_grouped_entry_with_own_kv_heads_matches_plain_call():
     assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(lse2, lse)
     for a, b in zip(got, plain):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.expects_timeout
+def test_grouped_timeout_writes_nan():
+    """A grouped call whose dQ wait runs out writes NaN into dq and into the
+    group-summed dk and dv (the group sum reads the call's failure flag)."""
+    c = GCase(1, 4, 2, 512, 64, False, 57)
+    ws = dab.alloc_workspace(c.B, c.H, c.S, c.D, False, "naive", 0, Hkv=c.Hkv)
+    say("grouped timeout path: poisoned counter, wait bound 2000 iterations")
+    try:
+        dab.set_wait_limit(2000, poison=True)
+        dq, dk, dv = dab.bwd(c.q, c.k, c.v, c.o, c.do, c.lse, False, "naive", workspace=ws)
+        torch.cuda.synchronize()
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert bool(torch.isnan(t.float()).all()), f"{name} of a call whose wait ran out is not all NaN"
+        with pytest.raises(dab.AttnError):
+            dab.check_workspace(ws)
+    finally:
+        dab.set_wait_limit(0, poison=False)
+    assert dab.wait_timeouts(reset=True) >= 1
+    dq, dk, dv = c.run("naive")
+    assert not bool(torch.isnan(dk.float()).any())
