@@ -180,6 +180,26 @@ def _bwd(q, k, v, o, do, lse, causal, schedule, scale, tile_request, workspace, 
     return dq, dk, dv
 
 
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool, schedule="naive", scale: float | None = None,
+                tile_request: int = 0, out=None):
+    """attn_bwd_deterministic_noalloc: the deterministic backward with the library's static
+    scratch as its workspace (no device allocation in the call when `out` is given); plain
+    heads only. Calls that overlap in time on one device race (they share the scratch)."""
+    torch = _torch()
+    B, H, Hkv, S, D = _check_heads(q, k, v, o, do)
+    if Hkv != H:
+        raise ValueError("bwd_noalloc takes one K/V head per query head")
+    _check_lse(lse, q.shape)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    mask = MASK_CAUSAL if causal else MASK_FULL
+    st = _lib.load().attn_bwd_deterministic_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), mask,
+                                                    _sched(schedule), _ptr(dq), _ptr(dk), _ptr(dv), B, H, S, D,
+                                                    scale, int(tile_request), _stream_ptr(q.device))
+    _lib.check(st, "attn_bwd_deterministic_noalloc")
+    return dq, dk, dv
+
+
 def check_workspace(workspace) -> None:
     """Synchronise the current stream; raise AttnError if a dQ ordering wait timed out."""
     st = _lib.load().attn_bwd_check(_ptr(workspace), workspace.numel(), _stream_ptr(workspace.device))

@@ -20,6 +20,8 @@ ERR_WORKSPACE = -3
 ERR_ALIGNMENT = -4
 ERR_HIP = -5
 ERR_TIMEOUT = -6
+ERR_SCRATCH_LIMIT = -7
+NOALLOC_SCRATCH_BYTES = 128 << 20  # ATTN_NOALLOC_SCRATCH_MIB
 
 MASK_FULL, MASK_CAUSAL = 0, 1
 SCHED_NAIVE, SCHED_DESCENDING, SCHED_SHIFT, SCHED_SYMMETRIC_SHIFT = 0, 1, 2, 3
@@ -31,6 +33,7 @@ EXPORTS = (
     "attn_bwd_workspace_size",
     "attn_bwd_deterministic",
     "attn_bwd_nondeterministic",
+    "attn_bwd_deterministic_noalloc",
     "attn_bwd_check",
     "attn_fwd_gqa",
     "attn_bwd_gqa_workspace_size",
@@ -94,6 +97,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.attn_bwd_deterministic.restype = i
     lib.attn_bwd_nondeterministic.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.attn_bwd_nondeterministic.restype = i
+    lib.attn_bwd_deterministic_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.attn_bwd_deterministic_noalloc.restype = i
     lib.attn_bwd_check.argtypes = [vp, sz, vp]
     lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_fwd_gqa.restype = i

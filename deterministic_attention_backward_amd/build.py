@@ -20,7 +20,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libattn_det.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.cpp", "bwd.hip", "fwd.hip", "probe.hip"]
+SOURCES = ["api.cpp", "bwd.hip", "fwd.hip", "probe.hip", "noalloc.hip"]
 PROFILE_LIB_PATH = os.path.join(PKG_DIR, "libattn_det_profile.so")
 
 # Packed-fp32 instructions are kept out of generated code on purpose.

@@ -87,6 +87,10 @@ int num_cu_current(int* out) {
   return ATTN_OK;
 }
 
+}  // namespace
+
+namespace attn {
+
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
             int mask, int schedule, void* dq, void* dk, void* dv, int B, int H, int Hkv, int S, int D, float scale,
             int tile_request, void* workspace, size_t workspace_bytes, void* stream, bool deterministic) {
@@ -125,7 +129,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-}  // namespace
+}  // namespace attn
 
 extern "C" {
 
@@ -138,6 +142,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIGNMENT: return "pointer not 16-byte aligned (workspace: 256-byte)";
     case ATTN_ERR_HIP: return "HIP runtime error";
     case ATTN_ERR_TIMEOUT: return "dQ ordering wait timed out";
+    case ATTN_ERR_SCRATCH_LIMIT: return "problem too large for the allocation-free entry point's static scratch";
     default: return "unknown status";
   }
 }

@@ -88,6 +88,12 @@ struct FwdArgs {
 inline int bwd_sub_rows(int D, int T) { return (D == 64 && T == 128) ? 128 : 64; }
 
 hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream);
+
+// The backward entry points' common path (api.cpp): validates every argument
+// on the host before any HIP call, then launches on `stream`. Returns a status.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, int mask,
+            int schedule, void* dq, void* dk, void* dv, int B, int H, int Hkv, int S, int D, float scale,
+            int tile_request, void* workspace, size_t workspace_bytes, void* stream, bool deterministic);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

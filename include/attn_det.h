@@ -49,7 +49,8 @@ typedef enum {
   ATTN_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required      */
   ATTN_ERR_ALIGNMENT = -4,     /* a pointer is not 16-byte aligned                */
   ATTN_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed      */
-  ATTN_ERR_TIMEOUT = -6        /* a dQ ordering wait exceeded its bound            */
+  ATTN_ERR_TIMEOUT = -6,       /* a dQ ordering wait exceeded its bound            */
+  ATTN_ERR_SCRATCH_LIMIT = -7  /* problem too large for attn_bwd_deterministic_noalloc */
 } attn_status_t;
 
 typedef enum { ATTN_MASK_FULL = 0, ATTN_MASK_CAUSAL = 1 } attn_mask_t;
@@ -129,6 +130,28 @@ int attn_bwd_nondeterministic(const void* q, const void* k, const void* v, const
                               void* dq, void* dk, void* dv, int B, int H, int S, int D,
                               float scale, int tile_request, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_deterministic_noalloc - attn_bwd_deterministic for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The call takes no workspace and
+ * makes no allocation: its workspace is a static device array of this
+ * library, ATTN_NOALLOC_SCRATCH_MIB MiB per device, held from the library's
+ * first use on a device until the process ends. Arguments, layout, results
+ * and bits are those of attn_bwd_deterministic (same kernels, same order).
+ * Problems whose workspace (attn_bwd_workspace_size) exceeds the array return
+ * ATTN_ERR_SCRATCH_LIMIT before any HIP call; 128 MiB covers, e.g., B=4,
+ * H=16, S=2048, D=128 (68 MB). Every call on one device shares that device's
+ * array: calls that overlap in time on one device (other streams or host
+ * threads) race and must not be issued; consecutive calls on one stream are
+ * fine. attn_bwd_check does not apply (there is no caller workspace); an
+ * expired wait still shows as NaN outputs.
+ */
+#define ATTN_NOALLOC_SCRATCH_MIB 128
+int attn_bwd_deterministic_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, int mask, int schedule,
+                                   void* dq, void* dk, void* dv, int B, int H, int S, int D,
+                                   float scale, int tile_request, void* stream);
 
 /*
  * attn_bwd_check - wait for `stream`, then report whether a deterministic call

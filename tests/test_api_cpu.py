@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(-6, 1):
+    for st in range(-7, 1):
         assert _lib.status_string(st) not in ("", "unknown status")
     assert _lib.status_string(-99) == "unknown status"
 
@@ -109,6 +109,32 @@ def test_validation_before_any_hip_call():
     assert call_det(ws=None) == _lib.ERR_WORKSPACE
     assert call_det(ws_bytes=1024) == _lib.ERR_WORKSPACE
     assert call_det(ws=ctypes.c_void_p((1 << 20) + 16)) == _lib.ERR_ALIGNMENT
+
+
+def call_noalloc(**over):
+    lib = _lib.load()
+    p = FakePtr()
+    args = dict(q=p(1), k=p(2), v=p(3), o=p(4), dout=p(5), lse=p(6), mask=0, schedule=0, dq=p(7), dk=p(8),
+                dv=p(9), B=1, H=2, S=256, D=64, scale=0.125, tile=0, stream=None)
+    args.update(over)
+    return lib.attn_bwd_deterministic_noalloc(*args.values())
+
+
+def test_noalloc_validation_before_any_hip_call():
+    # the allocation-free entry point validates like the workspace one, then refuses
+    # problems whose workspace exceeds its static scratch, all before any HIP call
+    assert call_noalloc(q=None) == _lib.ERR_INVALID_ARG
+    assert call_noalloc(B=0) == _lib.ERR_INVALID_ARG
+    assert call_noalloc(D=96) == _lib.ERR_UNSUPPORTED
+    assert call_noalloc(schedule=_lib.SCHED_SYMMETRIC_SHIFT, mask=_lib.MASK_FULL) == _lib.ERR_UNSUPPORTED
+    assert call_noalloc(dk=ctypes.c_void_p((1 << 20) + 8)) == _lib.ERR_ALIGNMENT
+    lib = _lib.load()
+    # 4 x 32 x 4096 x 128: the fp32 dQ accumulator alone is 256 MiB
+    assert lib.attn_bwd_workspace_size(4, 32, 4096, 128, 1, 2, 0) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(B=4, H=32, S=4096, D=128, mask=1, schedule=2) == _lib.ERR_SCRATCH_LIMIT
+    # the largest sizes it takes are stated in the header: 4 x 16 x 2048 x 128 fits
+    assert lib.attn_bwd_workspace_size(4, 16, 2048, 128, 0, 2, 0) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert "static scratch" in _lib.status_string(_lib.ERR_SCRATCH_LIMIT)
 
 
 def test_fwd_validation():
