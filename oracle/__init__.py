@@ -13,13 +13,17 @@ Contents:
     (ascending, Descending Q-Tile, Shift, Symmetric Shift) as task lists and
     accumulation orders, plus the DAG model: critical path, conflict freedom,
     Lemma 1 depth monotonicity and deadlock freedom.
+  * ``makespan`` - that DAG run for many heads on a fixed number of
+    processors fed from one ticket queue (the persistent grid's setting):
+    makespan, per-unit spans, busy and waiting time, deadlock detection.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things the
 oracle does not compute itself: finite differences, closed forms, invariants,
 torch's float64 autograd and ``scaled_dot_product_attention``, brute force
-over tiny cases, and hand-worked inputs (including ones that must be
-rejected) for the checkers ``attention.compare``, ``schedule.coverage_ok``,
+over tiny cases, list-scheduling bounds, a hand-worked two-head makespan
+golden, and hand-worked inputs (including ones that must be rejected) for
+the checkers ``attention.compare``, ``schedule.coverage_ok``,
 ``schedule.chains_ok`` and ``schedule.conflict_free``.
 """
 
-from . import attention, schedule  # noqa: F401
+from . import attention, makespan, schedule  # noqa: F401

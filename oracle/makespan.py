@@ -1,0 +1,145 @@
+"""Makespan of a dQ schedule over several heads on a fixed number of processors (test infrastructure).
+
+Only tests use this module. It extends the one-head DAG of the DASH pages
+(Dutch and Japanese technical summaries, §2.1: a compute node C(i,j) and a
+reduction node R(i,j) per task, each worker one unbroken chain, the dQ
+accumulation order adding R -> R edges) to a persistent grid that runs many
+heads: P identical processors take "units" (one worker of one head) from a
+single ticket queue, in ticket order, each as soon as it is free, and run a
+unit's chain to its end before taking the next ticket. A reduction that
+reaches its turn early holds its processor until the previous contribution
+to the same dQ tile has finished. §2.2 A of both summaries is about exactly
+this setting: with several heads in flight, the idle time a head's short
+workers leave behind (its "gaps") is taken by the next head's units.
+
+Readings (the pages do not spell the multi-head setting out):
+* processors free at the same instant take tickets in processor order;
+* a processor is held while its unit waits for a dQ turn (a workgroup of the
+  persistent kernel spins; it does not switch units);
+* the heads are independent: no edge joins two heads.
+
+With at least as many processors as units every unit starts at time 0 and
+the model is the pages' one-head DAG, so its makespan is that DAG's critical
+path. With fewer processors, a unit can wait for a unit holding a later
+ticket that no processor will ever take (every processor held by a waiting
+unit): the model reports that deadlock as None.
+"""
+
+from __future__ import annotations
+
+import heapq
+
+from . import schedule as Sch
+
+
+def ticket_order(plan: Sch.Plan, heads: int, worker_order=None):
+    """Head-major ticket list [(head, worker)]: all workers of head 0 in
+    worker_order (default ascending), then head 1, and so on."""
+    order = list(range(len(plan.workers))) if worker_order is None else list(worker_order)
+    if sorted(order) != list(range(len(plan.workers))):
+        raise ValueError("worker_order must be a permutation of the plan's workers")
+    return [(h, w) for h in range(heads) for w in order]
+
+
+def simulate(plan: Sch.Plan, heads: int, processors: int, c: float = 1.0, r: float = 0.0,
+             tickets=None):
+    """Run every unit of `heads` copies of `plan` on `processors` processors.
+
+    tickets: the queue as a list of (head, worker), default ticket_order(plan, heads).
+    Returns a dict with the makespan, each unit's (processor, start, end), and
+    each processor's busy and waiting time, or None if the run deadlocks.
+    """
+    if processors < 1:
+        raise ValueError("need at least one processor")
+    tickets = ticket_order(plan, heads) if tickets is None else list(tickets)
+    # predecessor of task (i, j) in dQ tile i's accumulation order (None for the first)
+    pred = {}
+    for i, order in enumerate(plan.orders):
+        for k, j in enumerate(order):
+            pred[(i, j)] = order[k - 1] if k else None
+    chains = [[(i, j) for _, i, j in sorted(tasks)] for tasks in plan.workers]
+
+    done = {}             # (head, i, j) -> finish time of R(i, j)
+    waiting = {}          # (head, i, j) -> the unit waiting for that reduction (its one successor)
+    units = []            # per started unit: [head, worker, processor, task index, start, ready time]
+    spans = {}
+    wait_time = [0.0] * processors
+    next_ticket = 0
+    events = []           # (time, kind, tie, seq, payload); kind 0 = R done, 1 = C done, 2 = processor free
+    seq = 0
+
+    def push(t, kind, tie, payload):
+        nonlocal seq
+        heapq.heappush(events, (t, kind, tie, seq, payload))
+        seq += 1
+
+    for p in range(processors):
+        push(0.0, 2, p, p)
+
+    while events:
+        t, kind, _, _, x = heapq.heappop(events)
+        if kind == 2:                         # processor x takes the next ticket
+            if next_ticket >= len(tickets):
+                continue
+            h, w = tickets[next_ticket]
+            next_ticket += 1
+            if not chains[w]:
+                spans[(h, w)] = (x, t, t)
+                push(t, 2, x, x)
+                continue
+            units.append([h, w, x, 0, t, None])
+            push(t + c, 1, x, len(units) - 1)
+        elif kind == 1:                       # unit x finished C of its current task
+            h, w, p, k, _, _ = units[x]
+            i, j = chains[w][k]
+            units[x][5] = t
+            before = pred[(i, j)]
+            if before is None or (h, i, before) in done:
+                # events run in time order: a finished predecessor finished by now
+                push(t + r, 0, p, x)
+            else:
+                waiting[(h, i, before)] = x
+        else:                                 # unit x finished R of its current task
+            h, w, p, k, start, _ = units[x]
+            i, j = chains[w][k]
+            done[(h, i, j)] = t
+            y = waiting.pop((h, i, j), None)
+            if y is not None:
+                wait_time[units[y][2]] += t - units[y][5]
+                push(t + r, 0, units[y][2], y)
+            if k + 1 < len(chains[w]):
+                units[x][3] = k + 1
+                push(t + c, 1, p, x)
+            else:
+                spans[(h, w)] = (p, start, t)
+                push(t, 2, p, p)
+
+    if waiting or next_ticket < len(tickets) or len(spans) != len(tickets):
+        return None
+    busy = [0.0] * processors
+    for (h, w), (p, s, e) in spans.items():
+        busy[p] += e - s
+    return {
+        "makespan": max((e for _, _, e in spans.values()), default=0.0),
+        "spans": spans,
+        "busy": busy,
+        "wait": wait_time,
+    }
+
+
+def makespan(plan: Sch.Plan, heads: int, processors: int, c: float = 1.0, r: float = 0.0, tickets=None):
+    """The makespan alone (None on deadlock)."""
+    res = simulate(plan, heads, processors, c, r, tickets)
+    return None if res is None else res["makespan"]
+
+
+def best_worker_order(plan: Sch.Plan, heads: int, processors: int, candidates: dict, c: float = 1.0,
+                      r: float = 0.0):
+    """Among named worker orders {name: order}, the one with the smallest
+    makespan (ties: first in the dict), and every candidate's makespan."""
+    results = {}
+    for name, order in candidates.items():
+        results[name] = makespan(plan, heads, processors, c, r, ticket_order(plan, heads, order))
+    finite = {k: v for k, v in results.items() if v is not None}
+    best = min(finite, key=lambda k: (finite[k], list(candidates).index(k))) if finite else None
+    return best, results
