@@ -103,27 +103,89 @@ def time_variant(fn, steps, warmup, torch, events, lib):
 KERNEL_SOURCES = ("bwd.hip", "common.hpp", "lds.hpp", "schedule.hpp", "launch.hpp")
 
 
-def measured_traffic(workload: str, schedule: str, protocol: str):
-    """HBM bytes per launch of the main kernel from the committed counter record.
-
-    profiles/bwd_main_<workload>_traffic.json holds FETCH_SIZE + WRITE_SIZE
-    (scaled by a 1 GiB copy) for one workload/schedule, with a hash of the
-    kernel sources it was taken on. Returns None unless it matches this run and
-    the sources are unchanged since.
-    """
+def kernel_source_hash() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"bwd_main_{workload}_traffic.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "deterministic_attention_backward_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if (rec.get("kernel_source_sha256") != h.hexdigest() or not rec.get("workload", "").startswith(workload + ":")
+    return h.hexdigest()
+
+
+def traffic_path(workload: str, schedule: str) -> str:
+    return os.path.join(ROOT, "profiles", f"bwd_main_{workload}_{schedule}_traffic.json")
+
+
+def measured_traffic(workload: str, schedule: str, protocol: str):
+    """HBM bytes per launch of the main kernel from the committed counter record.
+
+    profiles/bwd_main_<workload>_<schedule>_traffic.json holds FETCH_SIZE +
+    WRITE_SIZE (scaled by a 1 GiB copy) for one workload and schedule, with a
+    hash of the kernel sources it was taken on. Returns None unless it matches
+    this run and the sources are unchanged since.
+    """
+    path = traffic_path(workload, schedule)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if (rec.get("kernel_source_sha256") != kernel_source_hash() or not rec.get("workload", "").startswith(workload + ":")
             or rec.get("schedule") != schedule or rec.get("dq_protocol") != protocol):
         return None
     return float(rec["traffic_bytes"])
+
+
+def make_traffic_record(args):
+    """Write the traffic record of one workload/schedule from two rocprofv3 --pmc
+    runs of this script (FETCH_SIZE, then WRITE_SIZE, both with --copy-calibration):
+    per-dispatch means of the main kernel, each scaled by what the same counter
+    reads on the three 1 GiB device copies of the same run."""
+    import csv
+    import attn_inputs
+
+    def read(d, counter):
+        rows = []
+        for name in os.listdir(d):
+            if name.endswith("counter_collection.csv"):
+                rows += [r for r in csv.DictReader(open(os.path.join(d, name))) if r["Counter_Name"] == counter]
+        main = [r for r in rows if "bwd_main_kernel" in r["Kernel_Name"]]
+        kinds = sorted({r["Kernel_Name"] for r in main})
+        if len(kinds) != 1:
+            raise SystemExit(f"{d}: expected one main-kernel instantiation, found {kinds}")
+        # the copies run last, after every timed call: the last three dispatches of a non-library kernel
+        other = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rows
+                       if "attn::" not in r["Kernel_Name"])
+        copies = [v for _, v in other[-3:]]
+        vals = [float(r["Counter_Value"]) for r in main]
+        return kinds[0], len(vals), sum(vals) / len(vals), sum(copies) / len(copies)
+
+    fetch_dir, write_dir = args.make_traffic_record
+    w = attn_inputs.WORKLOADS[args.workload]
+    sched = args.schedules
+    kernel, n_f, fetch_kib, fetch_cal = read(fetch_dir, "FETCH_SIZE")
+    kernel_w, n_w, write_kib, write_cal = read(write_dir, "WRITE_SIZE")
+    if kernel != kernel_w:
+        raise SystemExit("the two runs timed different kernels")
+    gib = 1 << 30
+    fscale = gib / (fetch_cal * 1024)
+    wscale = gib / (write_cal * 1024)
+    fetch_b = fetch_kib * 1024 * fscale
+    write_b = write_kib * 1024 * wscale
+    rec = {"workload": f"{w.name}: {w.describe()}", "schedule": sched, "dq_protocol": args.dq_protocol,
+           "kernel": kernel, "dispatches": min(n_f, n_w),
+           "fetch_size_kib_per_dispatch": round(fetch_kib, 1), "write_size_kib_per_dispatch": round(write_kib, 1),
+           "copy_calibration": {"bytes": gib, "fetch_size_kib": round(fetch_cal, 1), "write_size_kib": round(write_cal, 1),
+                                "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
+           "fetch_bytes": int(fetch_b), "write_bytes": int(write_b), "traffic_bytes": int(fetch_b + write_b),
+           "kernel_source_sha256": kernel_source_hash(),
+           "command": f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch_dir> -o f -- python3 "
+                      f"<repo>/bench.py --workload {w.name} --also '' --schedules {sched} --steps 3 --warmup 1 "
+                      f"--cpu-seconds 0 --no-mfma-probe --no-nondet --copy-calibration; the same with --pmc "
+                      f"WRITE_SIZE into <write_dir>; then python3 <repo>/bench.py --workload {w.name} --schedules "
+                      f"{sched} --make-traffic-record <fetch_dir> <write_dir>"}
+    with open(traffic_path(w.name, sched), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, inputs, o_cpu, lse_cpu, budget_s: float):
@@ -206,20 +268,29 @@ def wait_profile(w, sched, args, torch, dab, _lib, tensors):
         for _ in range(2):
             dab.bwd(q, k, v, o, do, lse, w.causal, sched, w.scale, w.tile, ws)
         torch.cuda.synchronize()
-        buf = (ctypes.c_uint64 * (6 * 1024))()
+        K = _lib.WAIT_PROFILE_VALUES
+        buf = (ctypes.c_uint64 * (K * 1024))()
         n = prof.attn_debug_wait_profile(buf, 1024)
         _lib.check(min(n, 0), "attn_debug_wait_profile")
         bad = prof.attn_debug_order_violations(1)
         _lib.check(min(bad, 0), "attn_debug_order_violations")
     finally:
         _lib._lib = saved
-    rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
-    tot = [sum(r[j] for r in rows) for j in range(6)]
+    rows = [[buf[K * g + j] for j in range(K)] for g in range(n)]
+    tot = [sum(r[j] for r in rows) for j in range(K)]
     return {"schedule": sched, "workgroups": n,
             "tile_waves_barrier_frac": round(tot[0] / max(tot[1], 1), 4),
+            "tile_waves_kv_switch_frac": round(tot[6] / max(tot[1], 1), 4),
+            "tile_waves_claim_frac": round(tot[8] / max(tot[1], 1), 4),
             "dq_waves_turn_wait_frac": round(tot[2] / max(tot[4], 1), 4),
             "dq_waves_barrier_frac": round(tot[3] / max(tot[4], 1), 4),
             "turn_wait_cycles_per_subtile": round(tot[2] / max(tot[5], 1), 1),
+            "tile_wave_cycles_per_subtile": round(tot[1] / max(tot[5], 1), 1),
+            "cycles_per_kv_switch": round(tot[6] / max(tot[7], 1), 1),
+            "segments": tot[7], "subtiles": tot[5],
+            # the kernel lasts as long as its longest workgroup: mean / max of the
+            # workgroups' spans is the fraction of the grid kept busy to the end
+            "wg_span_mean_over_max": round(sum(r[1] for r in rows) / max(n * max(r[1] for r in rows), 1), 4),
             "dq_order_violations": bad,
             "note": "s_memtime cycles of one tile wave and one dQ wave per workgroup, profiling build"}
 
@@ -369,6 +440,9 @@ def main():
                     help="time an 8B-class attention block (forward + backward) instead; prints its own JSON line")
     ap.add_argument("--wait-profile", action="store_true",
                     help="one extra, untimed call of the best schedule with the profiling build: wait-cycle fractions")
+    ap.add_argument("--make-traffic-record", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/bwd_main_<workload>_<schedule>_traffic.json from two rocprofv3 --pmc runs "
+                         "(no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -379,6 +453,11 @@ def main():
         sys.exit(2)
     if args.block:
         block_bench(args)
+        return
+    if args.make_traffic_record:
+        if not args.schedules or "," in args.schedules:
+            raise SystemExit("--make-traffic-record needs one --schedules name")
+        make_traffic_record(args)
         return
 
     import torch

@@ -22,6 +22,7 @@ ERR_HIP = -5
 ERR_TIMEOUT = -6
 ERR_SCRATCH_LIMIT = -7
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ATTN_NOALLOC_SCRATCH_MIB
+WAIT_PROFILE_VALUES = 9  # uint64 values per workgroup from attn_debug_wait_profile
 
 MASK_FULL, MASK_CAUSAL = 0, 1
 SCHED_NAIVE, SCHED_DESCENDING, SCHED_SHIFT, SCHED_SYMMETRIC_SHIFT = 0, 1, 2, 3

@@ -196,11 +196,16 @@ __device__ __forceinline__ void lds_barrier() {
 //   [0] tile waves at the two hand-over barriers  [1] tile waves in total
 //   [2] dQ waves waiting for their dQ turn         [3] dQ waves at the barriers
 //   [4] dQ waves in total                          [5] sub-tiles handed off
+//   [6] tile waves switching KV tiles: a segment's set-up (K/V loads, parked
+//       accumulators restored, first sub-tile staged, three barriers) and
+//       tear-down (accumulators parked or dK/dV stored)
+//   [7] segments run                               [8] tile waves claiming units
 #ifndef ATTN_PROFILE_WAIT
 #define ATTN_PROFILE_WAIT 0
 #endif
 constexpr bool kProfileWait = ATTN_PROFILE_WAIT != 0;
-__device__ unsigned long long g_wait_prof[kMaxGrid][6];
+constexpr int kProfSlots = 9;
+__device__ unsigned long long g_wait_prof[kMaxGrid][kProfSlots];
 // Profiling build: dQ ordering checks. A wave that waits for its turn must
 // never see its flag beyond its rank (someone handed over out of order), and
 // a wave that hands over must find its flag still at its own rank (nobody
@@ -209,7 +214,7 @@ __device__ unsigned g_order_violations;
 static int g_last_grid = 0;
 
 struct WaitClock {
-  unsigned long long turn = 0, bar = 0;
+  unsigned long long turn = 0, bar = 0, seg = 0, nseg = 0, claim = 0;
 };
 __device__ __forceinline__ unsigned long long wclock() {
   if constexpr (kProfileWait) return __builtin_amdgcn_s_memtime();
@@ -497,10 +502,12 @@ struct TileRole {
         qv[(n + 1) & 1][0] = trB<G::RB>(QB, 0, tb, nx);
         qv[(n + 1) & 1][1] = trB<G::RB>(QB, 1, tb, nx);
       }
-      dVa[n] = mfma32(pb0, ov[n & 1][0], dVa[n]);
-      dVa[n] = mfma32(pb1, ov[n & 1][1], dVa[n]);
-      dKa[n] = mfma32(db0, qv[n & 1][0], dKa[n]);
-      dKa[n] = mfma32(db1, qv[n & 1][1], dKa[n]);
+      // dO^T P and Q^T dS: the accumulators hold dV^T and dK^T blocks, so a
+      // lane owns four consecutive features of one key per register quad
+      dVa[n] = mfma32(ov[n & 1][0], pb0, dVa[n]);
+      dVa[n] = mfma32(ov[n & 1][1], pb1, dVa[n]);
+      dKa[n] = mfma32(qv[n & 1][0], db0, dKa[n]);
+      dKa[n] = mfma32(qv[n & 1][1], db1, dKa[n]);
       if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -557,31 +564,41 @@ struct TileRole {
       park(sg, false);
       return;
     }
-    const int S = p.S;
+    // accumulator quad g of block n: features 32 n + 8 g + 4 hh + 0..3 of key l32
+    const int key = sg.kv * G::T + 32 * a + l32;
     if (p.dkv) {  // grouped-query heads: this query head's share, summed over the group later
-      float* pk = p.dkv + (size_t)sg.bh * p.S_pad * G::D;
+      float* pk = p.dkv + (size_t)sg.bh * p.S_pad * G::D + (size_t)key * G::D + 4 * hh;  // key < S_pad
       float* pv = pk + (size_t)p.BH * p.S_pad * G::D;
 #pragma unroll
       for (int n = 0; n < ND; ++n) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = sg.kv * G::T + 32 * a + 8 * (i / 4) + 4 * hh + (i % 4);
-          const size_t off = (size_t)key * G::D + 32 * n + l32;  // key < S_pad
-          pk[off] = dKa[n][i] * p.scale;
-          pv[off] = dVa[n][i];
+        for (int g = 0; g < 4; ++g) {
+          f32x4 kq, vq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kq[e] = dKa[n][4 * g + e] * p.scale;
+            vq[e] = dVa[n][4 * g + e];
+          }
+          *(f32x4*)(pk + 32 * n + 8 * g) = kq;
+          *(f32x4*)(pv + 32 * n + 8 * g) = vq;
         }
       }
       return;
     }
+    if (key < p.S) {
+      const size_t row = ((size_t)sg.bh * p.S + key) * G::D + 4 * hh;
 #pragma unroll
-    for (int n = 0; n < ND; ++n) {
+      for (int n = 0; n < ND; ++n) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = sg.kv * G::T + 32 * a + 8 * (i / 4) + 4 * hh + (i % 4);
-        if (key < S) {
-          const size_t off = ((size_t)sg.bh * S + key) * G::D + 32 * n + l32;
-          p.dk[off] = to_bf16(dKa[n][i] * p.scale);
-          p.dv[off] = to_bf16(dVa[n][i]);
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 kq, vq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kq[e] = to_bf16(dKa[n][4 * g + e] * p.scale);
+            vq[e] = to_bf16(dVa[n][4 * g + e]);
+          }
+          *(bf16x4*)(p.dk + row + 32 * n + 8 * g) = kq;
+          *(bf16x4*)(p.dv + row + 32 * n + 8 * g) = vq;
         }
       }
     }
@@ -901,6 +918,7 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
   const unsigned long long t_start = wclock();
   unsigned long long n_sub = 0;
   for (;;) {
+    const unsigned long long c0 = wclock();
     lds_barrier();
     if (threadIdx.x == 0) {
       if (!XCD) {
@@ -938,8 +956,16 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       }
     }
     lds_barrier();
+    if constexpr (kProfileWait) wclk.claim += wclock() - c0;
     const int bh = __builtin_amdgcn_readfirstlane(sUnit[0]);
-    const int wk = __builtin_amdgcn_readfirstlane(sUnit[1]);
+    // Causal Shift: dQ tile i receives KV tiles i, i-1, ..., 0 in that order,
+    // so worker j waits on worker j+1 at every step. Dealing a head's workers
+    // last KV tile first starts every predecessor before its successor; in
+    // ascending order the workers of a head that start one after another (as
+    // a previous head's shortest units drain) line up on the same dQ tiles
+    // and their hand-offs serialise.
+    const int wk_pos = __builtin_amdgcn_readfirstlane(sUnit[1]);
+    const int wk = (CAUSAL && p.sched == SCHED_SHIFT) ? p.n_workers - 1 - wk_pos : wk_pos;
     if (bh >= p.BH) break;
     const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
 
@@ -977,12 +1003,14 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       if (isA) parkedA = sg.keep;
       else parkedB = sg.keep;
 
+      const unsigned long long s0 = wclock();
       role.seg_begin(sg);  // tile waves: K/V, K^T to LDS, accumulators; dQ waves: load sub-tile 0
       lds_barrier();
       role.seg_kd(sg);     // dQ waves: K columns from LDS
       lds_barrier();
       role.seg_stage(sg);  // dQ waves: sub-tile 0 into LDS, load sub-tile 1
       lds_barrier();
+      const unsigned long long s1 = wclock();
       for (int i = 0; i < sg.n; ++i) {
         role.part1(sg, i);
         const unsigned long long b0 = wclock();
@@ -996,7 +1024,12 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
           ++n_sub;
         }
       }
+      const unsigned long long s2 = wclock();
       role.seg_end(sg);    // tile waves: park or write dK/dV; dQ waves: last sub-tile's dQ
+      if constexpr (kProfileWait) {
+        wclk.seg += (s1 - s0) + (wclock() - s2);
+        ++wclk.nseg;
+      }
       t0 = t1;
     }
   }
@@ -1007,6 +1040,9 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       if (wave == 0) {
         g_wait_prof[blockIdx.x][0] = wclk.bar;
         g_wait_prof[blockIdx.x][1] = total;
+        g_wait_prof[blockIdx.x][6] = wclk.seg;
+        g_wait_prof[blockIdx.x][7] = wclk.nseg;
+        g_wait_prof[blockIdx.x][8] = wclk.claim;
       } else if (wave == G::NA) {
         g_wait_prof[blockIdx.x][2] = wclk.turn;
         g_wait_prof[blockIdx.x][3] = wclk.bar;
@@ -1288,12 +1324,12 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
 extern "C" int attn_debug_wait_profile(uint64_t* out, int max_workgroups) {
   if (!attn::kProfileWait) return ATTN_ERR_UNSUPPORTED;
   if (!out || max_workgroups <= 0) return ATTN_ERR_INVALID_ARG;
-  static unsigned long long rows[attn::kMaxGrid][6];
+  static unsigned long long rows[attn::kMaxGrid][attn::kProfSlots];
   if (hipDeviceSynchronize() != hipSuccess) return ATTN_ERR_HIP;
   if (hipMemcpyFromSymbol(rows, HIP_SYMBOL(attn::g_wait_prof), sizeof(rows)) != hipSuccess) return ATTN_ERR_HIP;
   const int n = attn::g_last_grid < max_workgroups ? attn::g_last_grid : max_workgroups;
   for (int g = 0; g < n; ++g)
-    for (int k = 0; k < 6; ++k) out[6 * g + k] = rows[g][k];
+    for (int k = 0; k < attn::kProfSlots; ++k) out[attn::kProfSlots * g + k] = rows[g][k];
   return n;
 }
 

@@ -274,12 +274,16 @@ int attn_probe_mfma(int iterations, void* stream, double* tflops, double* ghz);
  * (libattn_det_profile.so, compiled with ATTN_PROFILE_WAIT=1); the regular
  * build returns ATTN_ERR_UNSUPPORTED. Synchronises the device, then writes,
  * for each workgroup of the last backward launch (at most max_workgroups),
- * six uint64 values: tile-wave cycles at the two per-sub-tile hand-over
- * barriers, tile-wave total cycles, dQ-wave cycles waiting for their dQ turn,
- * dQ-wave cycles at the barriers, dQ-wave total cycles, sub-tiles processed
- * (cycles of the s_memtime counter, one wave of each kind). Returns the
- * number of workgroups written (>= 0) or a negative status.
+ * ATTN_WAIT_PROFILE_VALUES (nine) uint64 values, cycles of the s_memtime
+ * counter of one wave of each kind unless noted: [0] tile-wave cycles at the
+ * two per-sub-tile hand-over barriers, [1] tile-wave total cycles, [2] dQ-wave
+ * cycles waiting for their dQ turn, [3] dQ-wave cycles at the barriers,
+ * [4] dQ-wave total cycles, [5] sub-tiles processed (a count), [6] tile-wave
+ * cycles switching KV tiles (segment set-up and tear-down), [7] segments run
+ * (a count), [8] tile-wave cycles claiming units. Returns the number of
+ * workgroups written (>= 0) or a negative status.
  */
+#define ATTN_WAIT_PROFILE_VALUES 9
 int attn_debug_wait_profile(uint64_t* out, int max_workgroups);
 
 /*

@@ -23,6 +23,12 @@ the model is the pages' one-head DAG, so its makespan is that DAG's critical
 path. With fewer processors, a unit can wait for a unit holding a later
 ticket that no processor will ever take (every processor held by a waiting
 unit): the model reports that deadlock as None.
+
+simulate_pipelined() is a second reading, closer to a kernel that overlaps
+the dQ hand-off with the next sub-tile's compute: the reduction runs off the
+processor, tasks may be cut into sub-tiles, a unit pays a set-up cost, and
+the processor may run a bounded number of sub-tiles ahead of its hand-offs.
+At its defaults it is simulate() exactly.
 """
 
 from __future__ import annotations
@@ -143,3 +149,148 @@ def best_worker_order(plan: Sch.Plan, heads: int, processors: int, candidates: d
     finite = {k: v for k, v in results.items() if v is not None}
     best = min(finite, key=lambda k: (finite[k], list(candidates).index(k))) if finite else None
     return best, results
+
+
+def simulate_pipelined(plan: Sch.Plan, heads: int, processors: int, c: float = 1.0, r: float = 0.0,
+                       tickets=None, nsub: int = 1, lag: int = 0, setup: float = 0.0, delay: float = 0.0,
+                       gate: str = "done"):
+    """The same queue and processors, with the reduction taken off the processor.
+
+    A reading of how a persistent kernel overlaps the dQ hand-off with compute
+    (the pages' DAG charges the reduction to the worker's chain): each task is
+    cut into `nsub` sub-tiles of compute time c each; sub-tile h of task (i, j)
+    contributes to dQ sub-tile (i, h), in the same KV order as the task. A
+    sub-tile's hand-off starts (takes its turn) no earlier than `delay` after
+    its compute has finished, once the unit's previous hand-off is done (a unit
+    hands over in order) and the previous contributor to the same dQ sub-tile
+    has finished its hand-off; it lasts r. The processor runs at most `lag`
+    sub-tiles ahead of its hand-offs: compute of sub-tile x waits until
+    hand-off x - 1 - lag has finished (gate "done") or started (gate "start":
+    the processor waits for the turn to be taken, not for the add). A unit
+    first spends `setup` on its own (loading its KV tile) and holds its
+    processor until its last hand-off is done.
+
+    With the defaults (nsub = 1, lag = 0, setup = 0, delay = 0, gate "done")
+    this is simulate(): the next task's compute waits for the previous
+    reduction, which then occupies the chain exactly as in the DAG. Returns the
+    same dict (or None on deadlock).
+    """
+    if processors < 1 or nsub < 1 or lag < 0 or gate not in ("done", "start"):
+        raise ValueError("need processors >= 1, nsub >= 1, lag >= 0, gate 'done' or 'start'")
+    tickets = ticket_order(plan, heads) if tickets is None else list(tickets)
+    pred = {}
+    for i, order in enumerate(plan.orders):
+        for k, j in enumerate(order):
+            pred[(i, j)] = order[k - 1] if k else None
+    chains = [[(i, j, hf) for _, i, j in sorted(tasks) for hf in range(nsub)] for tasks in plan.workers]
+
+    done = {}       # (head, i, half, j) -> hand-off finish time
+    waiting = {}    # (head, i, half, j) -> unit whose next hand-off follows that one
+    units = []      # dicts per started unit
+    spans = {}
+    wait_time = [0.0] * processors
+    next_ticket = 0
+    events = []     # (time, kind, tie, seq, payload)
+    seq = 0
+    # kinds: 0 hand-off done, 1 compute done, 2 processor free, 3 set-up done, 4 hand-off may start
+
+    def push(t, kind, tie, payload):
+        nonlocal seq
+        heapq.heappush(events, (t, kind, tie, seq, payload))
+        seq += 1
+
+    def try_compute(u, t):
+        """Start unit u's next compute at time t if the lag allows it."""
+        st = units[u]
+        x = st["nc"]
+        if st["busy_c"] or not st["ready"] or x >= len(st["chain"]):
+            return
+        need = x - 1 - lag           # the hand-off the processor may not run ahead of
+        passed = st["nh"] + (1 if (gate == "start" and st["busy_h"]) else 0)
+        if need >= 0 and passed <= need:
+            return
+        st["busy_c"] = True
+        push(t + c, 1, st["p"], u)
+
+    def try_handoff(u, t):
+        """Start unit u's next hand-off at time t if its conditions hold."""
+        st = units[u]
+        x = st["nh"]
+        if st["busy_h"] or x >= len(st["chain"]) or x not in st["may"]:
+            return
+        i, j, hf = st["chain"][x]
+        before = pred[(i, j)]
+        key = (st["h"], i, hf, before)
+        if before is not None and key not in done:
+            waiting[key] = u
+            st["wait_from"] = t
+            return
+        st["busy_h"] = True
+        push(t + r, 0, st["p"], u)
+        try_compute(u, t)
+
+    for p in range(processors):
+        push(0.0, 2, p, p)
+
+    while events:
+        t, kind, _, _, x = heapq.heappop(events)
+        if kind == 2:                                   # processor x takes the next ticket
+            if next_ticket >= len(tickets):
+                continue
+            h, w = tickets[next_ticket]
+            next_ticket += 1
+            if not chains[w]:
+                spans[(h, w)] = (x, t, t)
+                push(t, 2, x, x)
+                continue
+            units.append({"h": h, "w": w, "p": x, "start": t, "chain": chains[w], "nc": 0, "nh": 0,
+                          "may": set(), "busy_c": False, "busy_h": False, "ready": setup <= 0,
+                          "wait_from": None})
+            u = len(units) - 1
+            if setup > 0:
+                push(t + setup, 3, x, u)
+            else:
+                try_compute(u, t)
+        elif kind == 3:                                 # unit x finished its set-up
+            units[x]["ready"] = True
+            try_compute(x, t)
+        elif kind == 1:                                 # unit x finished computing sub-tile nc
+            st = units[x]
+            st["nc"] += 1
+            st["busy_c"] = False
+            if delay > 0:
+                push(t + delay, 4, st["p"], (x, st["nc"] - 1))
+            else:
+                st["may"].add(st["nc"] - 1)
+                try_handoff(x, t)
+            try_compute(x, t)
+        elif kind == 4:                                 # a finished sub-tile's hand-off may start
+            u, y = x
+            units[u]["may"].add(y)
+            try_handoff(u, t)
+        else:                                           # unit x finished hand-off nh
+            st = units[x]
+            i, j, hf = st["chain"][st["nh"]]
+            key = (st["h"], i, hf, j)
+            done[key] = t
+            st["nh"] += 1
+            st["busy_h"] = False
+            y = waiting.pop(key, None)
+            if y is not None:
+                wait_time[units[y]["p"]] += t - units[y]["wait_from"]
+                units[y]["wait_from"] = None
+                try_handoff(y, t)
+            if st["nh"] == len(st["chain"]):
+                spans[(st["h"], st["w"])] = (st["p"], st["start"], t)
+                push(t, 2, st["p"], st["p"])
+            else:
+                try_handoff(x, t)
+                try_compute(x, t)
+
+    if waiting or next_ticket < len(tickets) or len(spans) != len(tickets):
+        return None
+    busy = [0.0] * processors
+    for (h, w), (p, s, e) in spans.items():
+        busy[p] += e - s
+    return {"makespan": max((e for _, _, e in spans.values()), default=0.0), "spans": spans, "busy": busy,
+            "wait": wait_time}

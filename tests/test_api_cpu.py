@@ -35,6 +35,15 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    want = {"ATTN_WAIT_PROFILE_VALUES": _lib.WAIT_PROFILE_VALUES,
+            "ATTN_NOALLOC_SCRATCH_MIB": _lib.NOALLOC_SCRATCH_BYTES >> 20}
+    for name, value in want.items():
+        m = re.search(rf"^#define\s+{name}\s+(\d+)", text, re.M)
+        assert m and int(m.group(1)) == value, name
+
+
 def test_status_strings():
     for st in range(-7, 1):
         assert _lib.status_string(st) not in ("", "unknown status")

@@ -15,6 +15,8 @@ from deterministic_attention_backward_amd import _lib
 
 pytestmark = pytest.mark.gpu
 
+K = _lib.WAIT_PROFILE_VALUES
+
 
 def test_mfma_probe_is_plausible():
     lib = _lib.load()
@@ -26,7 +28,7 @@ def test_mfma_probe_is_plausible():
     # dense bf16 peak of the part is about 2.5 PFLOP/s at 2.4 GHz
     assert 100.0 < tf.value < 3000.0
     assert 0.3 < ghz.value < 3.5
-    assert lib.attn_debug_wait_profile((ctypes.c_uint64 * 6)(), 1) == _lib.ERR_UNSUPPORTED
+    assert lib.attn_debug_wait_profile((ctypes.c_uint64 * _lib.WAIT_PROFILE_VALUES)(), 1) == _lib.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("causal,sched", [(False, "shift"), (True, "symmetric_shift"), (True, "naive")])
@@ -43,16 +45,19 @@ def test_profiling_build_is_bitwise_identical(causal, sched):
         _lib._lib = prof
         got = dab.bwd(q, k, v, o, do, lse, causal, sched)
         torch.cuda.synchronize()
-        buf = (ctypes.c_uint64 * (6 * 1024))()
+        buf = (ctypes.c_uint64 * (K * 1024))()
         n = prof.attn_debug_wait_profile(buf, 1024)
     finally:
         _lib._lib = saved
     for a, b in zip(ref, got):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert n > 0
-    rows = [[buf[6 * g + j] for j in range(6)] for g in range(n)]
+    rows = [[buf[K * g + j] for j in range(K)] for g in range(n)]
     assert sum(r[5] for r in rows) > 0            # sub-tiles were counted
+    assert sum(r[7] for r in rows) > 0            # and segments
     assert all(r[2] <= r[4] and r[0] <= r[1] for r in rows)  # waits are part of the total
+    # barriers, KV-tile switches and unit claims are disjoint parts of the tile wave's time
+    assert all(r[0] + r[6] + r[8] <= r[1] for r in rows)
 
 
 @pytest.mark.parametrize("protocol", ["xcd_local", "device"])

@@ -5,7 +5,11 @@ so reproduce the hand-derived critical-path closed forms; a hand-worked
 two-head golden (tests/golden/makespan_two_heads.json) that includes the gap
 §2.2 A of the Dutch and Japanese technical summaries speaks of; bounds any
 list schedule obeys (total work over P, the longest chain, one processor
-running everything in sequence); and deadlock cases worked out by hand.
+running everything in sequence); and deadlock cases worked out by hand. The
+pipelined reading (hand-off off the processor) is pinned by reducing to the
+DAG model at its defaults, by a closed form for full-mask Shift, by a
+hand-worked golden (tests/golden/makespan_pipelined.json), and by the proof
+sketched at test_causal_shift_last_tile_first_never_waits.
 """
 
 import json
@@ -115,8 +119,8 @@ def test_ticket_order_validation():
 
 # Per-XCD shapes of the benchmark workloads: one XCD's queue holds B*H/8 heads and its
 # 32 workgroups are the processors (one resident workgroup per CU at D = 128). The kernel
-# deals a head's workers in ascending KV-tile order; the model finds no better order among
-# the two natural ones for any schedule at these shapes.
+# deals a head's workers in ascending KV-tile order except for causal Shift; for the other
+# schedules the model finds no better order among the two natural ones at these shapes.
 XCD_SHAPES = [  # (N, causal, heads per XCD)
     (16, False, 8),    # B=4, H=16, S=2048 full
     (32, True, 16),    # B=4, H=32, S=4096 causal
@@ -126,8 +130,10 @@ XCD_SHAPES = [  # (N, causal, heads per XCD)
 
 @pytest.mark.parametrize("N,causal,heads", XCD_SHAPES)
 def test_ascending_worker_order_is_never_worse(N, causal, heads):
+    # causal Shift is the exception, covered below: its dQ chains run from the
+    # last KV tile down, and the kernel deals its workers in that order
     for sched in (Sch.NAIVE, Sch.DESCENDING, Sch.SHIFT, Sch.SYMMETRIC_SHIFT):
-        if sched == Sch.SYMMETRIC_SHIFT and not causal:
+        if (sched == Sch.SYMMETRIC_SHIFT and not causal) or (sched == Sch.SHIFT and causal):
             continue
         plan = Sch.build(N, causal, sched)
         n = len(plan.workers)
@@ -135,3 +141,88 @@ def test_ascending_worker_order_is_never_worse(N, causal, heads):
             best, res = M.best_worker_order(plan, heads, 32, {"ascending": range(n), "descending": range(n)[::-1]},
                                             1.0, r)
             assert best == "ascending", (Sch.NAMES[sched], r, res)
+
+
+# ---- the pipelined reading (the hand-off runs off the processor)
+
+@pytest.mark.parametrize("N,causal,sched", [x for x in cases() if x[0] in (1, 2, 3, 4, 6)])
+def test_pipelined_defaults_are_the_dag_model(N, causal, sched):
+    plan = Sch.build(N, causal, sched)
+    n = len(plan.workers)
+    for heads, P in ((1, n), (2, n), (3, n + 1), (2, max(1, n - 1))):
+        for c, r in WEIGHTS:
+            a = M.simulate(plan, heads, P, c, r)
+            b = M.simulate_pipelined(plan, heads, P, c, r)
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert a["spans"] == b["spans"] and a["wait"] == b["wait"]
+
+
+def test_pipelined_full_shift_closed_form():
+    # conflict-free steps and a hand-off no longer than a compute: every hand-off
+    # overlaps the next compute, so one head takes its N nsub computes plus the
+    # last hand-off
+    for N in (2, 4, 8):
+        plan = Sch.build(N, False, Sch.SHIFT)
+        for nsub in (1, 2):
+            for r in (0.0, 0.5, 1.0):
+                for gate in ("done", "start"):
+                    res = M.simulate_pipelined(plan, 1, N, 1.0, r, nsub=nsub, lag=1, gate=gate)
+                    assert res["makespan"] == pytest.approx(N * nsub + r)
+                    assert sum(res["wait"]) == 0.0
+                # a set-up before the first compute and a delay before each hand-off
+                # (no longer than a compute) add once; every unit spans the whole run
+                for setup, delay in ((2.0, 0.0), (0.0, 0.5), (3.0, 1.0)):
+                    res = M.simulate_pipelined(plan, 1, N, 1.0, r, nsub=nsub, lag=1, setup=setup, delay=delay,
+                                               gate="start")
+                    want = setup + N * nsub + delay + r
+                    assert res["makespan"] == pytest.approx(want)
+                    assert all(sp == (w, 0.0, pytest.approx(want)) for w, (sp) in
+                               zip(range(N), [res["spans"][(0, w)] for w in range(N)]))
+
+
+def test_golden_pipelined():
+    g = json.load(open(os.path.join(GOLDEN, "makespan_pipelined.json")))
+    plan = Sch.build(2, True, Sch.SHIFT)
+    for case in g["cases"]:
+        res = M.simulate_pipelined(plan, 2, 2, 1.0, 1.0, M.ticket_order(plan, 2, case["worker_order"]), nsub=1,
+                                   lag=1, gate="start")
+        assert res["makespan"] == case["makespan"], case["name"]
+        assert sum(res["wait"]) == case["wait"], case["name"]
+        assert res["spans"] == {(h, w): (p, s, e) for h, w, p, s, e in case["spans"]}, case["name"]
+
+
+PIPE_PARAMS = [  # (c, r, delay, lag, setup, nsub, gate)
+    (1.0, 0.0, 0.0, 0, 0.0, 1, "done"), (1.0, 1.0, 0.0, 0, 0.0, 1, "done"), (1.0, 0.25, 0.0, 0, 0.0, 1, "done"),
+    (1.0, 0.5, 1.0, 1, 3.0, 2, "start"), (1.0, 1.0, 1.0, 1, 3.0, 2, "start"), (2.0, 1.0, 1.0, 1, 0.0, 2, "done"),
+    (1.0, 1.0, 0.5, 1, 0.0, 1, "start"), (1.0, 1.0, 1.0, 2, 1.0, 2, "start"),
+]
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 5, 8, 12])
+def test_causal_shift_last_tile_first_never_waits(N):
+    # causal Shift's dQ tile i takes KV tiles i, i-1, ..., 0, so worker j waits on
+    # worker j+1. Dealt last KV tile first, worker j+1 starts no later than worker j
+    # and is one task ahead on every dQ tile they share, so (by induction from the
+    # last worker, which is always first on its tiles) no hand-off ever waits
+    plan = Sch.build(N, True, Sch.SHIFT)
+    order = list(range(N))[::-1]
+    for P in (N, N + 1, N + N // 2, 2 * N):
+        for heads in (1, 2, 3, 5):
+            res = M.simulate(plan, heads, P, 1.0, 1.0, M.ticket_order(plan, heads, order))
+            assert sum(res["wait"]) == 0.0
+            for c, r, delay, lag, setup, nsub, gate in PIPE_PARAMS:
+                res = M.simulate_pipelined(plan, heads, P, c, r, M.ticket_order(plan, heads, order), nsub=nsub,
+                                           lag=lag, setup=setup, delay=delay, gate=gate)
+                assert sum(res["wait"]) == 0.0, (P, heads, c, r, delay, lag, setup, nsub, gate)
+
+
+def test_causal_shift_first_tile_first_waits_at_the_kernel_shape():
+    # ascending tickets: the next head's workers start one after another as the
+    # previous head's shortest units drain, each after its own predecessor in the
+    # dQ chain, so hand-offs wait (the kernel measures these waits as a large loss)
+    plan = Sch.build(32, True, Sch.SHIFT)
+    for c, r, delay, lag, setup, nsub, gate in PIPE_PARAMS[3:5]:
+        res = M.simulate_pipelined(plan, 16, 32, c, r, None, nsub=nsub, lag=lag, setup=setup, delay=delay,
+                                   gate=gate)
+        assert sum(res["wait"]) > 0.0
