@@ -252,7 +252,9 @@ def repeat_check(fn, runs, torch):
 
 
 def rnd(x):
-    return {k: round(v, 4) for k, v in x.items()} if isinstance(x, dict) else round(x, 4)
+    if isinstance(x, dict):
+        return {k: rnd(v) for k, v in x.items()}
+    return round(x, 4) if isinstance(x, float) else x
 
 
 def wait_profile(w, sched, args, torch, dab, _lib, tensors):
@@ -391,7 +393,12 @@ def measure(w, args, torch, dab, _lib, lib, events):
         ws = dab.alloc_workspace(w.B, w.H, w.S, w.D, w.causal, "naive", w.tile, Hkv=w.kv_heads)
         fn = lambda: dab.bwd_nondeterministic(q, k, v, o, do, lse, w.causal, w.scale, w.tile, ws, out)
         ms, kms, api = time_variant(fn, args.steps, args.warmup, torch, events, lib)
-        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api}
+        # one fp32 atomic add per element of every task's dQ partial (T rows x D per task)
+        tasks = N * (N + 1) // 2 if w.causal else N * N
+        adds = w.B * w.H * tasks * T * w.D
+        nondet = {"ms": ms, "kernel_ms": kms, "tflops": w.flops / (ms * 1e-3) / 1e12, "api_ms": api,
+                  "walk": "shift", "placement": "per-XCD head queue",
+                  "atomic_adds_per_launch": adds, "atomic_gops": adds / (kms * 1e-3) / 1e9}
         log(f"  {'atomic (non-det)':16s} {ms:8.3f} ms/call  main kernel {kms:8.3f} ms  {nondet['tflops']:7.1f} TFLOP/s")
         del ws
     best = min(results, key=lambda s: results[s]["ms"])
@@ -485,6 +492,22 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {nbytes} bytes read + {nbytes} bytes written per copy, 3 copies")
 
+    atomic_probe = None
+    if not args.no_nondet and not args.no_mfma_probe:
+        buf = torch.zeros(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB, about C3F's dQ accumulator
+        g = ctypes.c_double()
+        _lib.check(lib.attn_probe_atomic(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, 200,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), ctypes.byref(g)),
+                   "attn_probe_atomic")
+        del buf
+        atomic_probe = {"gops": round(g.value, 1),
+                        "probe": "fp32 atomic adds, 64 consecutive floats per instruction, 4 KB blocks, one block "
+                                 "per wave at a time, 256 MiB buffer"}
+        log(f"measured fp32 atomic-add rate {g.value:.1f} Gop/s")
+        for rec in [head] + list(subs.values()):
+            if rec.get("nondet"):
+                rec["nondet"]["atomic_bound_frac"] = round(rec["nondet"]["atomic_gops"] / g.value, 4)
+
     mfma = None
     if not args.no_mfma_probe:
         tf, ghz = ctypes.c_double(), ctypes.c_double()
@@ -519,6 +542,7 @@ def main():
     for key in ("schedules", "dq_wait_timeouts", "bitwise_identical_runs", "nondet"):
         line[key] = head[key]
     line["mfma_measured"] = mfma
+    line["atomic_measured"] = atomic_probe
     line["pct_measured_mfma_peak"] = round(100.0 * head["value"] / mfma["tflops"], 2) if mfma else None
     line["roofline"] = head["roofline"]
     line["sub_records"] = subs

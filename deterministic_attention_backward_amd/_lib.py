@@ -45,6 +45,7 @@ EXPORTS = (
     "attn_set_timing_events",
     "attn_debug_set_dq_protocol",
     "attn_probe_mfma",
+    "attn_probe_atomic",
     "attn_debug_wait_profile",
     "attn_debug_wait_timeouts",
     "attn_debug_order_violations",
@@ -122,6 +123,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.attn_debug_set_dq_protocol.restype = i
     lib.attn_probe_mfma.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     lib.attn_probe_mfma.restype = i
+    lib.attn_probe_atomic.argtypes = [vp, ctypes.c_size_t, i, vp, ctypes.POINTER(ctypes.c_double)]
+    lib.attn_probe_atomic.restype = i
     lib.attn_debug_wait_profile.argtypes = [ctypes.POINTER(ctypes.c_uint64), i]
     lib.attn_debug_wait_profile.restype = i
     lib.attn_debug_wait_timeouts.argtypes = [i]

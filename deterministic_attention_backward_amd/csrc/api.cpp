@@ -117,7 +117,12 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   a.T = sh.T; a.BR = sh.BR; a.N = sh.N; a.S_pad = sh.S_pad; a.n_qsub = sh.n_qsub;
   a.scale = scale;
   a.causal = mask == ATTN_MASK_CAUSAL;
-  a.sched = deterministic ? schedule : ATTN_SCHED_NAIVE;
+  // The atomic variant has no order to keep: it walks Shift's order, so that
+  // at every step the workers of a head add into different dQ tiles.
+#ifndef ATTN_ATOMIC_WALK
+#define ATTN_ATOMIC_WALK ATTN_SCHED_SHIFT
+#endif
+  a.sched = deterministic ? schedule : ATTN_ATOMIC_WALK;
   a.atomic = deterministic ? 0 : 1;
   a.wait_limit = g_wait_limit;
   a.poison = g_poison;

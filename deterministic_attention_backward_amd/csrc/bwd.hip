@@ -903,9 +903,16 @@ struct DqRole {
 #endif
 constexpr bool PASSES = ATTN_SUBTILE_PASSES != 0;
 
+#ifndef ATTN_ATOMIC_XCD_QUEUE
+#define ATTN_ATOMIC_XCD_QUEUE 1
+#endif
+
 template <class G, bool CAUSAL, int MODE, class Role>
 __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, Role& role) {
-  constexpr bool XCD = MODE == MODE_XCD;
+  // Per-XCD queues: the XCD-local hand-off needs every contributor of a head
+  // on one XCD; the atomic variant uses them too, so that a head's atomic
+  // adds land in one XCD's L2 (it never waits, so any placement is safe).
+  constexpr bool XCD = MODE == MODE_XCD || (MODE == MODE_ATOMIC && ATTN_ATOMIC_XCD_QUEUE != 0);
   int xq = 0;  // this workgroup's XCD, the queue it takes units from
   if (XCD) {
     unsigned x;
@@ -965,7 +972,7 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
     // a previous head's shortest units drain) line up on the same dQ tiles
     // and their hand-offs serialise.
     const int wk_pos = __builtin_amdgcn_readfirstlane(sUnit[1]);
-    const int wk = (CAUSAL && p.sched == SCHED_SHIFT) ? p.n_workers - 1 - wk_pos : wk_pos;
+    const int wk = (CAUSAL && p.sched == SCHED_SHIFT && MODE != MODE_ATOMIC) ? p.n_workers - 1 - wk_pos : wk_pos;
     if (bh >= p.BH) break;
     const int ntasks = sched_num_tasks(p.N, CAUSAL, p.sched, wk);
 

@@ -39,9 +39,58 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int iters, float seed, 
   }
 }
 
+// fp32 atomic-add throughput in the access pattern of the atomic-dQ variant:
+// each instruction adds into 64 consecutive floats (256 bytes), sixteen
+// instructions cover a 4 KB block, and every wave walks its own sequence of
+// blocks (no two waves on one block at a time).
+__global__ void __launch_bounds__(256) atomic_probe_kernel(float* buf, long long n_blocks, int iters) {
+  const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long long n_waves = (long long)gridDim.x * 4;
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < iters; ++it) {
+    const long long blk = (wave + (long long)it * n_waves) % n_blocks;
+    float* base = buf + blk * 1024 + lane;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) atomicAdd(base + 64 * e, 1.0f);
+  }
+}
+
 }  // namespace attn
 
 using namespace attn;
+
+extern "C" int attn_probe_atomic(void* buffer, size_t bytes, int iterations, void* stream, double* gops) {
+  if (!buffer || bytes < 4096 || iterations <= 0 || !gops) return ATTN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(buffer) & 255u) != 0) return ATTN_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0, num_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return ATTN_ERR_HIP;
+  const int grid = num_cu * 8;  // eight 4-wave workgroups per CU
+  const long long n_blocks = (long long)(bytes / 4096);
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return ATTN_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    hipEventDestroy(e0);
+    return ATTN_ERR_HIP;
+  }
+  int st = ATTN_OK;
+  float ms = 0.0f;
+  for (int rep = 0; rep < 2 && st == ATTN_OK; ++rep) {  // warm-up launch, then the timed one
+    if (rep == 1 && hipEventRecord(e0, s) != hipSuccess) st = ATTN_ERR_HIP;
+    hipLaunchKernelGGL(atomic_probe_kernel, dim3(grid), dim3(256), 0, s, static_cast<float*>(buffer), n_blocks,
+                       iterations);
+    if (hipGetLastError() != hipSuccess) st = ATTN_ERR_HIP;
+    if (rep == 1 && st == ATTN_OK && hipEventRecord(e1, s) != hipSuccess) st = ATTN_ERR_HIP;
+  }
+  if (st == ATTN_OK && hipEventSynchronize(e1) != hipSuccess) st = ATTN_ERR_HIP;
+  if (st == ATTN_OK && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) st = ATTN_ERR_HIP;
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (st != ATTN_OK) return st;
+  *gops = (double)grid * 4.0 * iterations * 16.0 * 64.0 / (ms * 1e-3) / 1e9;
+  return ATTN_OK;
+}
 
 extern "C" int attn_probe_mfma(int iterations, void* stream, double* tflops, double* ghz) {
   if (iterations <= 0 || !tflops || !ghz) return ATTN_ERR_INVALID_ARG;

@@ -270,6 +270,21 @@ void attn_set_timing_events(void* before, void* after);
 int attn_probe_mfma(int iterations, void* stream, double* tflops, double* ghz);
 
 /*
+ * attn_probe_atomic - measurement probe (not part of the backward): the fp32
+ * atomic-add throughput that bounds the non-deterministic variant, in that
+ * variant's access pattern (each instruction adds into 64 consecutive
+ * floats; 4 KB blocks; every wave on its own block). `buffer` is caller-owned
+ * device memory of `bytes` bytes (256-byte aligned, at least 4096), whose
+ * contents the probe overwrites with sums; eight 4-wave workgroups per CU
+ * each run `iterations` rounds of 16 adds per lane, after one warm-up
+ * launch, on `stream`, and the call waits for them. *gops receives atomic
+ * adds per second / 1e9. Returns ATTN_ERR_INVALID_ARG or ATTN_ERR_ALIGNMENT
+ * for bad arguments (checked before any HIP call), ATTN_ERR_HIP on a
+ * runtime error. Allocates nothing.
+ */
+int attn_probe_atomic(void* buffer, size_t bytes, int iterations, void* stream, double* gops);
+
+/*
  * attn_debug_wait_profile - only in the profiling build of the library
  * (libattn_det_profile.so, compiled with ATTN_PROFILE_WAIT=1); the regular
  * build returns ATTN_ERR_UNSUPPORTED. Synchronises the device, then writes,

@@ -44,6 +44,16 @@ def test_header_constants_match_the_binding():
         assert m and int(m.group(1)) == value, name
 
 
+def test_atomic_probe_validates_before_any_hip_call():
+    lib = _lib.load()
+    g = ctypes.c_double()
+    assert lib.attn_probe_atomic(None, 1 << 20, 10, None, ctypes.byref(g)) == _lib.ERR_INVALID_ARG
+    assert lib.attn_probe_atomic(ctypes.c_void_p(4096), 100, 10, None, ctypes.byref(g)) == _lib.ERR_INVALID_ARG
+    assert lib.attn_probe_atomic(ctypes.c_void_p(4096), 1 << 20, 0, None, ctypes.byref(g)) == _lib.ERR_INVALID_ARG
+    assert lib.attn_probe_atomic(ctypes.c_void_p(4096 + 16), 1 << 20, 10, None, ctypes.byref(g)) == _lib.ERR_ALIGNMENT
+    assert lib.attn_probe_atomic(ctypes.c_void_p(4096), 1 << 20, 10, None, None) == _lib.ERR_INVALID_ARG
+
+
 def test_status_strings():
     for st in range(-7, 1):
         assert _lib.status_string(st) not in ("", "unknown status")

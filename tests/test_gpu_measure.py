@@ -31,6 +31,20 @@ def test_mfma_probe_is_plausible():
     assert lib.attn_debug_wait_profile((ctypes.c_uint64 * _lib.WAIT_PROFILE_VALUES)(), 1) == _lib.ERR_UNSUPPORTED
 
 
+def test_atomic_probe_is_plausible():
+    lib = _lib.load()
+    buf = torch.zeros(1 << 22, dtype=torch.float32, device="cuda")  # 16 MiB: 4096 blocks of 4 KB
+    g = ctypes.c_double()
+    st = torch.cuda.current_stream().cuda_stream
+    assert lib.attn_probe_atomic(ctypes.c_void_p(buf.data_ptr()), buf.numel() * 4, 20, ctypes.c_void_p(st),
+                                 ctypes.byref(g)) == 0
+    assert 10.0 < g.value < 100000.0
+    # two launches (warm-up and timed) of 8 workgroups x 4 waves per CU, 20 rounds of 16 adds of 1.0 per lane
+    torch.cuda.synchronize()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert float(buf.sum()) == 2 * n_cu * 8 * 4 * 64 * 20 * 16
+
+
 @pytest.mark.parametrize("causal,sched", [(False, "shift"), (True, "symmetric_shift"), (True, "naive")])
 def test_profiling_build_is_bitwise_identical(causal, sched):
     B, H, S, D = 1, 4, 1024, 128
