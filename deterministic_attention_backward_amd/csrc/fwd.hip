@@ -12,7 +12,17 @@
 // row-wise (A operand of S^T), V through the transposing read (A operand of
 // O^T, rows in the C-row order of P^T). The DMA of tile t+1 is issued before
 // tile t is computed; one barrier per tile. Causal masks: a query tile stops
-// at its diagonal, and the grid takes the longest query tiles first.
+// at its diagonal. Only the tiles that cross the diagonal or the end of the
+// sequence evaluate masks, and the output accumulators are rescaled only when
+// some lane's running maximum grew (a factor of exactly 1 otherwise).
+//
+// Work order: workgroup L of the grid runs on XCD L mod 8, so the j-th
+// workgroup of an XCD takes query tile level j / (heads per XCD) (longest
+// first on a causal mask, over all heads) of one of that XCD's heads: a
+// head's K and V are read by one XCD's L2 only, and the grid drains longest
+// tiles first.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds.hpp"
@@ -26,11 +36,12 @@ struct FwdParams {
   int S;
   int H, group;  // query heads per batch; query heads per K/V head
   int n_qt;      // query tiles per head
+  int BH;        // batch x query heads
   float scale_log2;
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) fwd_kernel(FwdParams p) {
   constexpr int KT = 64;           // keys per tile
   constexpr int RB = 2 * D;        // staged row bytes
   constexpr int KC = D / 16;
@@ -42,9 +53,21 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = p.S;
-  const long long bh = blockIdx.y;
+  long long bh;
+  int level;
+  {
+    const int L = blockIdx.x;
+    if (p.BH % 8 == 0) {  // XCD-aware: XCD x owns heads x, x + 8, ...
+      const int hpx = p.BH / 8, x = L % 8, j = L / 8;
+      level = j / hpx;
+      bh = (long long)(j % hpx) * 8 + x;
+    } else {
+      level = L / p.BH;
+      bh = L % p.BH;
+    }
+  }
   // causal: the longest query tiles (the last ones) first
-  const int qt = CAUSAL ? p.n_qt - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int qt = CAUSAL ? p.n_qt - 1 - level : level;
   const int q0 = qt * 128;
   const int qrow = q0 + 32 * w + l32;   // this lane's query
   const bf16* qh = p.q + bh * S * D;
@@ -52,22 +75,41 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
   const bf16* kh = p.k + kvh * S * D;
   const bf16* vh = p.v + kvh * S * D;
 
-  // DMA of keys k0..k0+63 (K and V) into buffer buf; keys past the end are
-  // read as copies of the last key (the mask gives them P = 0 exactly)
-  auto stage = [&](int k0, int buf) {
-    constexpr int CPR = D / 8, RPP = 64 / CPR, HALF = PIECES / 2;
-    int rl = lane / CPR, lx = (lane % CPR) ^ swz<D>(lane / CPR);
-    asm volatile("" : "+v"(rl), "+v"(lx));
+  // DMA of keys k0..k0+63 (K and V) into buffer buf. Lane L of piece pr
+  // fetches row pr RPP + rl, chunk lx ^ swz(pr RPP): a byte offset fixed per
+  // piece (piece_off) from the tile's first row, so a full tile needs no
+  // per-lane address arithmetic. On the last, partial tile keys past the end
+  // are read as copies of the last key (the mask gives them P = 0 exactly).
+  constexpr int CPR = D / 8, RPP = 64 / CPR, HALF = PIECES / 2;
+  unsigned piece_off[PPW];
+  int piece_row[PPW];
+  {
+    const int rl = lane / CPR, lx = (lane % CPR) ^ swz<D>(lane / CPR);
+#pragma unroll
+    for (int k = 0; k < PPW; ++k) {
+      const int piece = w * PPW + k;
+      const int pr = piece >= HALF ? piece - HALF : piece;
+      piece_row[k] = pr * RPP + rl;
+      piece_off[k] = (unsigned)(piece_row[k] * RB + 16 * (lx ^ swz<D>(pr * RPP)));
+    }
+  }
+  auto stage_pieces = [&](int k0, int buf, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
     for (int k = 0; k < PPW; ++k) {
       const int piece = w * PPW + k;  // wave-uniform
       const bool is_v = piece >= HALF;
       const int pr = is_v ? piece - HALF : piece;
-      const unsigned off = (unsigned)(min(k0 + pr * RPP + rl, S - 1) * RB + 16 * (lx ^ swz<D>(pr * RPP)));
+      unsigned off = piece_off[k];
+      if constexpr (!FULL) off += (unsigned)((min(k0 + piece_row[k], S - 1) - k0 - piece_row[k]) * RB);
       char* dst = smem + (2 * buf + (is_v ? 1 : 0)) * TB + pr * 1024;
-      __builtin_amdgcn_global_load_lds(at_bytes(is_v ? vh : kh, off), (__attribute__((address_space(3))) void*)dst, 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(at_bytes((is_v ? vh : kh) + (size_t)k0 * D, off),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
+  };
+  auto stage = [&](int k0, int buf) {
+    if (k0 + KT <= S) stage_pieces(k0, buf, std::true_type{});  // workgroup-uniform
+    else stage_pieces(k0, buf, std::false_type{});
   };
 
   int kend = S;
@@ -89,6 +131,8 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int n = 0; n < ND; ++n) oacc[n] = zero16();
   float m = -__builtin_inff(), l = 0.0f;
+  const bool pos = p.scale_log2 >= 0.0f;
+  const float hidden = pos ? -__builtin_inff() : __builtin_inff();  // scaled by the scale: -inf
   const int sw = swz<D>(l32);
   const int a_base = l32 * RB + 16 * ((hh ^ sw) & 1), sw1 = sw >> 1;
   TrLane tl;
@@ -102,8 +146,9 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
     const char* Kb = smem + (2 * buf) * TB;
     const char* Vb = Kb + TB;
 
+    // raw scores S^T; on tiles crossing the diagonal or the end of the
+    // sequence, masked entries become the score whose scaled value is -inf
     f32x16 st[2];
-    float tmax = -__builtin_inff();
     int ab = a_base, s1 = sw1;
     asm volatile("" : "+v"(ab), "+v"(s1));
 #pragma unroll
@@ -112,38 +157,67 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
       f32x16 acc = zero16();
 #pragma unroll
       for (int c = 0; c < KC; ++c) acc = mfma32(*(const bf16x8*)(Kr + ((c ^ s1) << 5)), Qr[c], acc);
-      const bool edge = k0 + KT > S || (CAUSAL && k0 + KT > q0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
-        const bool vis = !edge || (key < S && (!CAUSAL || key <= qrow));
-        const float x = vis ? acc[i] * p.scale_log2 : -__builtin_inff();
-        acc[i] = x;
-        tmax = fmaxf(tmax, x);
-      }
       st[kb] = acc;
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = fast_exp2(m - mnew);
-    float psum = 0.0f;
+    // P = exp2(S scale log2(e) - m) with the running maximum m brought up to
+    // this tile, one fused multiply-add per score; the two instantiations keep
+    // the mask code off the tiles that need none
+    auto softmax = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
+      if constexpr (EDGE) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(st[kb][i] - mnew);
-        st[kb][i] = pv;
-        psum += pv;
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
+            if (!(key < S && (!CAUSAL || key <= qrow))) st[kb][i] = hidden;
+          }
+        }
       }
-    }
-    psum += __shfl_xor(psum, 32);
-    l = l * alpha + psum;
-    m = mnew;
+      // the row's largest scaled score: the largest raw score for a positive
+      // scale, the smallest for a negative one
+      float tsel = st[0][0];
+      if (pos) {
 #pragma unroll
-    for (int n = 0; n < ND; ++n) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[n][i] *= alpha;
-    }
+          for (int i = 0; i < 16; ++i) tsel = fmaxf(tsel, st[kb][i]);
+        tsel = fmaxf(tsel, __shfl_xor(tsel, 32));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tsel = fminf(tsel, st[kb][i]);
+        tsel = fminf(tsel, __shfl_xor(tsel, 32));
+      }
+      const float mnew = fmaxf(m, tsel * p.scale_log2);
+      float psum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = fast_exp2(__builtin_fmaf(st[kb][i], p.scale_log2, -mnew));
+          if constexpr (EDGE) {
+            if (st[kb][i] == hidden) pv = 0.0f;  // (a zero scale would make it NaN)
+          }
+          st[kb][i] = pv;
+          psum += pv;
+        }
+      }
+      psum += __shfl_xor(psum, 32);
+      // rescale by exp2(m - mnew): exactly 1 for the rows whose maximum did not
+      // grow (a branch around it costs as much, in copies of the accumulators)
+      const float alpha = fast_exp2(m - mnew);
+      l = l * alpha + psum;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[n][i] *= alpha;
+      }
+      m = mnew;
+    };
+    if (k0 + KT > S || (CAUSAL && k0 + KT > q0)) softmax(std::true_type{});  // workgroup-uniform
+    else softmax(std::false_type{});
     int tb[2] = {tl.base[0], tl.base[1]}, th = tl.hi;
     asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
 #pragma unroll
@@ -186,8 +260,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   fp.H = a.H;
   fp.group = a.H / a.Hkv;
   fp.n_qt = (a.S + 127) / 128;
+  fp.BH = a.B * a.H;
   fp.scale_log2 = a.scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)((a.S + 127) / 128), (unsigned)((long long)a.B * a.H));
+  const dim3 grid((unsigned)((long long)fp.n_qt * fp.BH));
   if (a.D == 64) {
     if (a.causal) hipLaunchKernelGGL((fwd_kernel<64, true>), grid, dim3(256), 0, stream, fp);
     else hipLaunchKernelGGL((fwd_kernel<64, false>), grid, dim3(256), 0, stream, fp);

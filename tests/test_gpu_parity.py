@@ -224,6 +224,26 @@ def test_workspace_reuse_sees_fresh_accumulators(sched):
             assert err <= 2e-2, f"{sched} seed {seed} {name}: {err:.3e}"
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.7], ids=["zero", "negative"])
+@pytest.mark.parametrize("case", [(1, 2, 300, 128, True, 83), (1, 2, 200, 64, False, 84)],
+                         ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "f"))
+def test_forward_with_a_zero_or_negative_scale(case, scale):
+    """The forward tracks the row maximum of the scaled scores: with a negative
+    scale that is the smallest raw score, and with a zero scale every visible
+    key gets the same weight while masked keys (the diagonal tiles and the
+    ragged tail) must still get none."""
+    B, H, S, D, causal, seed = case
+    scale = scale / math.sqrt(D)
+    say(f"forward with scale {scale:.4f}: B={B} H={H} S={S} D={D} causal={causal}")
+    x = attn_inputs.draw(B, H, S, D, seed)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = dab.fwd(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.forward(f64(q), f64(k), f64(v), causal, scale)
+    assert_close("O", f64(o), o_ref)
+    assert np.abs(f64(lse) - lse_ref).max() <= 1e-3
+
+
 @pytest.mark.parametrize("case", [(1, 3, 300, 128, True, 81), (2, 2, 256, 64, False, 82)],
                          ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3], "c" if c[4] else "f"))
 def test_parity_with_a_caller_softmax_scale(case):
