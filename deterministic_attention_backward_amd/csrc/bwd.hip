@@ -1018,7 +1018,11 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       role.seg_stage(sg);  // dQ waves: sub-tile 0 into LDS, load sub-tile 1
       lds_barrier();
       const unsigned long long s1 = wclock();
-      for (int i = 0; i < sg.n; ++i) {
+      // (sg.n >= 1: the body runs at least once, which also tells the
+      // compiler that the accumulators loaded in seg_begin have arrived by
+      // seg_end, so the epilogue's stores need no waits for them)
+      int i = 0;
+      do {
         role.part1(sg, i);
         const unsigned long long b0 = wclock();
         lds_barrier();  // X
@@ -1030,7 +1034,7 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
           wclk.bar += (b1 - b0) + (wclock() - b2);
           ++n_sub;
         }
-      }
+      } while (++i < sg.n);
       const unsigned long long s2 = wclock();
       role.seg_end(sg);    // tile waves: park or write dK/dV; dQ waves: last sub-tile's dQ
       if constexpr (kProfileWait) {
