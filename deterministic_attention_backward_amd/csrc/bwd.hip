@@ -585,22 +585,51 @@ struct TileRole {
       }
       return;
     }
-    if (key < p.S) {
-      const size_t row = ((size_t)sg.bh * p.S + key) * G::D + 4 * hh;
+    // bf16 dK and dV through LDS: this wave's own 32 rows of the K-row region
+    // (idle once the dQ waves have read K^T) take dK, and its rows of the
+    // V-row region (D = 128) or of a staging buffer (free between segments)
+    // take dV, written as the accumulators hold them (four features of one key
+    // per lane). Both are written first, which frees the accumulator
+    // registers; then they are read back along the rows, so that each store
+    // instruction writes whole rows (full cache lines) instead of a 16-byte
+    // piece of 32 rows.
+    // (per-lane base offsets made opaque here, so that the compiler does not
+    // hoist them out of the segment loop and keep them in spilled registers)
+    int wofs = (32 * a + l32) * G::DP + 4 * hh, rofs = (32 * a + lane / (G::D / 8)) * G::DP + 8 * (lane % (G::D / 8));
+    asm volatile("" : "+v"(wofs), "+v"(rofs));
+    bf16* stg_k = L.kt();
+    bf16* stg_v = G::V_LDS ? L.v() : (bf16*)L.q(0);
 #pragma unroll
-      for (int n = 0; n < ND; ++n) {
+    for (int n = 0; n < ND; ++n) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 kq, vq;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 k4, v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            kq[e] = to_bf16(dKa[n][4 * g + e] * p.scale);
-            vq[e] = to_bf16(dVa[n][4 * g + e]);
-          }
-          *(bf16x4*)(p.dk + row + 32 * n + 8 * g) = kq;
-          *(bf16x4*)(p.dv + row + 32 * n + 8 * g) = vq;
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = to_bf16(dKa[n][4 * g + e] * p.scale);
+          v4[e] = to_bf16(dVa[n][4 * g + e]);
         }
+        *(bf16x4*)(stg_k + wofs + 32 * n + 8 * g) = k4;
+        *(bf16x4*)(stg_v + wofs + 32 * n + 8 * g) = v4;
+        __builtin_amdgcn_sched_barrier(0);  // convert and write one quad at a time (registers)
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are written
+    constexpr int LPR = G::D / 8, RPI = 64 / LPR;  // lanes per row, rows per instruction
+    const int key0 = sg.kv * G::T + 32 * a;
+    const size_t out0 = ((size_t)sg.bh * p.S + key0) * G::D;  // wave-uniform
+    int grow = lane / LPR;                                      // this lane's row of the first instruction
+    unsigned gofs = (unsigned)(grow * G::D + 8 * (lane % LPR)) * 2u;
+    asm volatile("" : "+v"(grow), "+v"(gofs));
+#pragma unroll
+    for (int r = 0; r < 32 / RPI; ++r) {
+      const bf16x8 k8 = *(const bf16x8*)(stg_k + rofs + RPI * r * G::DP);
+      const bf16x8 v8 = *(const bf16x8*)(stg_v + rofs + RPI * r * G::DP);
+      if (key0 + grow + RPI * r < p.S) {
+        *at_bytes((bf16x8*)(p.dk + out0), gofs + (unsigned)(RPI * r * G::D * 2)) = k8;
+        *at_bytes((bf16x8*)(p.dv + out0), gofs + (unsigned)(RPI * r * G::D * 2)) = v8;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
