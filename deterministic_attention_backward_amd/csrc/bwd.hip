@@ -359,23 +359,40 @@ struct TileRole {
 
   __device__ __forceinline__ void seg_begin(const Seg& sg) {
     const int S = p.S;
-    const int key = min(sg.kv * G::T + 32 * a + l32, S - 1);  // keys past the end are masked
     // K/V head of this query head (grouped-query attention: group consecutive query heads share one)
     const int kvh = (sg.bh / p.H) * (p.H / p.group) + (sg.bh % p.H) / p.group;
     const bf16* kh = p.k + (size_t)kvh * S * G::D;
     const bf16* vh = p.v + (size_t)kvh * S * G::D;
+    // This wave's 32 K and V rows, loaded along the rows (each instruction
+    // reads whole rows: full cache lines) into the K-row region (which the
+    // dQ waves read transposed) and the V-row region (D = 64: a staging
+    // buffer the dQ waves fill only later), then this wave's K operand is
+    // read back in the MFMA layout. Keys past the end are read as copies of
+    // the last key (they are masked).
+    constexpr int LPR = G::D / 8, RPI = 64 / LPR, NR = 32 / RPI;  // lanes per row, rows per instruction
+    int lrow = lane / LPR, lcol = 8 * (lane % LPR);
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
+    const int key0 = sg.kv * G::T + 32 * a;
+    bf16x8 kq[NR], vq[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const unsigned off = 2u * (unsigned)(min(key0 + RPI * r + lrow, S - 1) * G::D + lcol);
+      kq[r] = *at_bytes((const bf16x8*)kh, off);
+      vq[r] = *at_bytes((const bf16x8*)vh, off);
+    }
+    bf16* kt = L.kt();
+    bf16* vs = VL ? L.v() : (bf16*)L.q(1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      *(bf16x8*)&kt[(32 * a + RPI * r + lrow) * G::DP + lcol] = kq[r];
+      *(bf16x8*)&vs[(32 * a + RPI * r + lrow) * G::DP + lcol] = vq[r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const unsigned off = 2u * (unsigned)(key * G::D + 16 * c + 8 * hh);
-      Kr[c] = *at_bytes((const bf16x8*)kh, off);
-      const bf16x8 vv = *at_bytes((const bf16x8*)vh, off);
-      if constexpr (VL) *(bf16x8*)&L.v()[(32 * a + l32) * G::DP + 16 * c + 8 * hh] = vv;
-      else Vr[VL ? 0 : c] = vv;
+      Kr[c] = *(const bf16x8*)&kt[(32 * a + l32) * G::DP + 16 * c + 8 * hh];
+      if constexpr (!VL) Vr[c] = *(const bf16x8*)&vs[(32 * a + l32) * G::DP + 16 * c + 8 * hh];
     }
-    // K rows for the dQ waves' operand (they read it transposed)
-    bf16* kt = L.kt();
-#pragma unroll
-    for (int c = 0; c < KC; ++c) *(bf16x8*)&kt[(32 * a + l32) * G::DP + 16 * c + 8 * hh] = Kr[c];
     if (sg.restore) {
       park(sg, true);
     } else {
