@@ -103,12 +103,40 @@ def time_variant(fn, steps, warmup, torch, events, lib):
 KERNEL_SOURCES = ("bwd.hip", "common.hpp", "lds.hpp", "schedule.hpp", "launch.hpp")
 
 
-def kernel_source_hash() -> str:
+def code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so that
+    edits of comments or layout do not invalidate measurements of the code."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':  # string literal (asm templates): copied as is
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the main kernel's sources (code only). `read(name)` returns a
+    file's text (default: the working tree)."""
     import hashlib
+    if read is None:
+        read = lambda f: open(os.path.join(ROOT, "deterministic_attention_backward_amd", "csrc", f)).read()
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "deterministic_attention_backward_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_only(read(f)).encode())
     return h.hexdigest()
 
 

@@ -105,8 +105,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(PreParams p) {
 // A workgroup holds one KV tile of T keys and runs two kinds of waves, one of
 // each per SIMD:
 //   tile waves (T/32): wave a owns keys 32a..32a+31. Its registers hold those
-//     keys' K and V rows (B operands of S = Q K^T and dP = dO V^T) and their dK
-//     and dV accumulators for the whole run of tasks on the tile. Per query
+//     keys' K rows (B operand of S = Q K^T; at D = 64 also the V rows of
+//     dP = dO V^T, which at D = 128 the wave reads from its own LDS rows) and
+//     their dK and dV accumulators (transposed: four consecutive features of
+//     one key per register quad) for the whole run of tasks on the tile. Per query
 //     sub-tile of BR rows it computes S, dP, P and dS, writes dS^T to LDS and
 //     accumulates dV += P^T dO and dK += dS^T Q, reading the staged Q and dO
 //     rows both row-wise (A operands) and transposed (B operands, through the

@@ -62,6 +62,20 @@ def test_make_traffic_record_arithmetic(tmp_path, monkeypatch):
     assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
 
 
+def test_source_hash_ignores_comments_and_layout_only():
+    src = 'int a = 1; // note\n/* block\n comment */  asm volatile("s_waitcnt vmcnt(0) // kept" ::: "memory");\n'
+    assert bench.code_only(src) == 'int a = 1; asm volatile("s_waitcnt vmcnt(0) // kept" ::: "memory");'
+    assert bench.code_only(src) == bench.code_only(src.replace("// note", "// other words").replace("  ", "\n\t"))
+    assert bench.code_only(src) != bench.code_only(src.replace("a = 1", "a = 2"))
+    texts = {f: open(os.path.join(ROOT, "deterministic_attention_backward_amd", "csrc", f)).read()
+             for f in bench.KERNEL_SOURCES}
+    h = bench.kernel_source_hash(lambda f: texts[f])
+    assert h == bench.kernel_source_hash()
+    first = bench.KERNEL_SOURCES[0]
+    assert bench.kernel_source_hash(lambda f: texts[f] + ("// x\n" if f == first else "")) == h
+    assert bench.kernel_source_hash(lambda f: texts[f] + ("int z;\n" if f == first else "")) != h
+
+
 def test_repeat_check_counts_identical_runs():
     a = torch.arange(12, dtype=torch.bfloat16)
     assert bench.repeat_check(lambda: (a, a, a), 20, torch) == 20
