@@ -309,12 +309,17 @@ struct Seg {
 #ifndef ATTN_TILE_PIPE
 #define ATTN_TILE_PIPE 1
 #endif
+#ifndef ATTN_TILE_ILV
+#define ATTN_TILE_ILV 1
+#endif
 
 template <class G, bool CAUSAL, int MODE>
 struct TileRole {
   static constexpr int KC = G::KC, ND = G::ND, MB = G::MB, NSUB = G::NSUB;
   // software-pipelined row blocks (D = 64: registers to spare for a second S/dP block)
   static constexpr bool PIPE = ATTN_TILE_PIPE != 0 && G::D == 64;
+  // D = 128: dS computed between the dV MFMAs (see probs .. dkeys)
+  static constexpr bool ILV = ATTN_TILE_ILV != 0 && !PIPE && G::ND == 4;
   const MainParams& p;
   Lds<G> L;
   int tid, lane, a, l32, hh;
@@ -326,6 +331,7 @@ struct TileRole {
   bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
   f32x16 s, dp;  // first row block of the current sub-tile, carried over barrier X
+  bf16x8 dsb[2];  // (D = 128 order: only its dS, packed, is carried over X)
   WaitClock* wc = nullptr;  // profiling build only
 
   __device__ __forceinline__ TileRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
@@ -531,6 +537,107 @@ struct TileRole {
     }
   }
 
+  // ---- D = 128 order. Row block m: S and dP (their MFMAs interleaved, as
+  // in mma()), then P in place; then dV^T += dO^T P with dS = P (dP - Delta)
+  // computed between those MFMAs (four scores per feature block), so that this
+  // vector work runs while they do; then dS^T to LDS and dK^T += Q^T dS. Only
+  // the packed dS of row block 0 is carried over barrier X. The arithmetic of
+  // every element is that of soft() and accumulate().
+
+  // P from S in place (soft()'s first half)
+  template <bool MASK>
+  __device__ __forceinline__ void probs(int m, int buf, int q_base, int kv_base, f32x16& sc) {
+    const float* Ls = L.lse(buf) + 32 * m + 4 * hh;
+    const int key_g = kv_base + 32 * a + l32;
+    const bool key_ok = key_g < p.S;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 L4 = *(const f32x4*)&Ls[8 * g];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * g + b;
+        float pv = fast_exp2(__builtin_fmaf(sc[i], p.scale_log2, -L4[b]));
+        if constexpr (MASK) {
+          const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
+          const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
+          pv = vis ? pv : 0.0f;
+        }
+        sc[i] = pv;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void dvalues(int m, int buf, const f32x16& sc, f32x16& dpr, bf16x8& d0, bf16x8& d1) {
+    const bf16x8 pb0 = pack8(sc, 0), pb1 = pack8(sc, 8);
+    int tb[2] = {tl.base[0], tl.base[1]}, th = tl.hi;
+    asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
+    const char* OB = L.o(buf) + 32 * m * G::RB;
+    const float* Ds = L.dl(buf) + 32 * m + 4 * hh;
+    bf16x8 ov[2][2];
+    {
+      const int nx = th << 6;
+      ov[0][0] = trB<G::RB>(OB, 0, tb, nx);
+      ov[0][1] = trB<G::RB>(OB, 1, tb, nx);
+    }
+    f32x4 D4[2];
+    D4[0] = *(const f32x4*)&Ds[0];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+      if (n + 1 < ND) {
+        const int nx = ((n + 1) ^ th) << 6;
+        ov[(n + 1) & 1][0] = trB<G::RB>(OB, 0, tb, nx);
+        ov[(n + 1) & 1][1] = trB<G::RB>(OB, 1, tb, nx);
+        D4[(n + 1) & 1] = *(const f32x4*)&Ds[8 * (n + 1)];
+      }
+      dVa[n] = mfma32(ov[n & 1][0], pb0, dVa[n]);
+      dVa[n] = mfma32(ov[n & 1][1], pb1, dVa[n]);
+      // dS of quad n of the block's rows
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dpr[4 * n + b] = sc[4 * n + b] * (dpr[4 * n + b] - D4[n & 1][b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    d0 = pack8(dpr, 0);
+    d1 = pack8(dpr, 8);
+  }
+
+  __device__ __forceinline__ void dkeys(int m, int buf, bf16x8 d0, bf16x8 d1) {
+    bf16* drow = &L.dst()[(32 * a + l32) * G::SP + 32 * m + 4 * hh];  // four consecutive queries per write
+    *(bf16x4*)(drow + 0) = __builtin_shufflevector(d0, d0, 0, 1, 2, 3);
+    *(bf16x4*)(drow + 8) = __builtin_shufflevector(d0, d0, 4, 5, 6, 7);
+    *(bf16x4*)(drow + 16) = __builtin_shufflevector(d1, d1, 0, 1, 2, 3);
+    *(bf16x4*)(drow + 24) = __builtin_shufflevector(d1, d1, 4, 5, 6, 7);
+    int tb[2] = {tl.base[0], tl.base[1]}, th = tl.hi;
+    asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
+    const char* QB = L.q(buf) + 32 * m * G::RB;
+    bf16x8 qv[2][2];
+    {
+      const int nx = th << 6;
+      qv[0][0] = trB<G::RB>(QB, 0, tb, nx);
+      qv[0][1] = trB<G::RB>(QB, 1, tb, nx);
+    }
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+      if (n + 1 < ND) {
+        const int nx = ((n + 1) ^ th) << 6;
+        qv[(n + 1) & 1][0] = trB<G::RB>(QB, 0, tb, nx);
+        qv[(n + 1) & 1][1] = trB<G::RB>(QB, 1, tb, nx);
+      }
+      dKa[n] = mfma32(qv[n & 1][0], d0, dKa[n]);
+      dKa[n] = mfma32(qv[n & 1][1], d1, dKa[n]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // a row block up to (not including) its dS write and dK products
+  __device__ __forceinline__ void block_front(int m, int buf, int q_base, int kv_base, bool need_mask, bf16x8& d0,
+                                              bf16x8& d1) {
+    f32x16 sc, dpr;
+    mma(m, buf, sc, dpr);
+    if (need_mask) probs<true>(m, buf, q_base, kv_base, sc);
+    else probs<false>(m, buf, q_base, kv_base, sc);
+    dvalues(m, buf, sc, dpr, d0, d1);
+  }
+
   __device__ __forceinline__ void where(const Seg& sg, int i, int& q_base, int& kv_base, bool& need_mask) {
     const Task task = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.task<NSUB>(i));
     q_base = task.q * G::T + sg.half<NSUB>(i) * G::BR;
@@ -542,14 +649,28 @@ struct TileRole {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    sdp(0, i & 1, q_base, kv_base, need_mask);
+    if constexpr (ILV) {
+      block_front(0, i & 1, q_base, kv_base, need_mask, dsb[0], dsb[1]);
+    } else {
+      sdp(0, i & 1, q_base, kv_base, need_mask);
+    }
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    if constexpr (PIPE) {
+    if constexpr (ILV) {
+      // (row block 0's dS is written only now: the dQ waves read the previous
+      // sub-tile's before barrier X)
+      dkeys(0, i & 1, dsb[0], dsb[1]);
+#pragma unroll
+      for (int m = 1; m < MB; ++m) {
+        bf16x8 d0, d1;
+        block_front(m, i & 1, q_base, kv_base, need_mask, d0, d1);
+        dkeys(m, i & 1, d0, d1);
+      }
+    } else if constexpr (PIPE) {
       // row block m+1's scores are issued before row block m's dV/dK
       // products, and its softmax follows them: with no scheduling fences the
       // compiler can interleave one block's VALU work with the other's MFMAs
@@ -714,7 +835,9 @@ struct DqRole {
     }
   }
   // the DMA issued by this wave (and every older vector memory operation) has completed
-  __device__ __forceinline__ static void stage_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+  // (the wait is a builtin, not inline asm, so that the compiler knows the
+  // staged rows have landed and puts no waits of its own before LDS reads)
+  __device__ __forceinline__ static void stage_wait() { wait_vmem(); }
 
   __device__ __forceinline__ int sub_row0(const Seg& sg, int i) const {
     const Task t = sched_task(p.N, CAUSAL, p.sched, sg.wk, sg.task<NSUB>(i));
@@ -745,7 +868,7 @@ struct DqRole {
       // latency hides behind that of the stores)
       int now = 0;
       if constexpr (kProfileWait) now = XCD ? l2_load(&p.flags[pend]) : sys_load(&p.flags[pend]);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmem();
       if constexpr (kProfileWait) {
         if (__builtin_amdgcn_readfirstlane(now) != pend_val - 1 && lane == 0) atomicAdd(&g_order_violations, 1u);
       }
@@ -775,10 +898,10 @@ struct DqRole {
     }
   }
 
-  __device__ __forceinline__ void seg_stage(const Seg& sg) {
-    stage_wait();  // sub-tile 0
-    if (sg.n > 1) stage(sg.bh, sub_row0(sg, 1), 1);
-  }
+  // Sub-tile 0 has landed. (Sub-tile 1 is staged inside the loop, by part1 of
+  // sub-tile 0: no DMA is then in flight where the loop is entered, so the
+  // compiler needs no wait of its own before the loop's LDS reads.)
+  __device__ __forceinline__ void seg_stage(const Seg&) { stage_wait(); }
 
   // The hand-off of sub-tile j runs in three steps spread over the next
   // interval so that its memory latencies overlap other work:
@@ -921,12 +1044,16 @@ struct DqRole {
   // is computed, and has landed before barrier Y.
   __device__ __forceinline__ void part1(const Seg& sg, int i) {
     if (i > 0) read_ds();
-    if (i >= 1 && i + 1 < sg.n) stage(sg.bh, sub_row0(sg, i + 1), (i + 1) & 1);
+    if (i + 1 < sg.n) stage(sg.bh, sub_row0(sg, i + 1), (i + 1) & 1);
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
-    // (the running sums of i-2 were loaded an interval ago)
-    if (i + 1 < sg.n) stage_wait();   // sub-tile i+1's rows
+    // sub-tile i+1's rows and the running sums of i-2 (loaded an interval
+    // ago). Waited for on every path, also where nothing was staged, so that
+    // the compiler sees no DMA in flight at the loop head and puts no wait of
+    // its own before the next dS reads (which would hold them, and the DMA
+    // issued after them, until the running-sum loads of this interval arrive).
+    stage_wait();
     if (i > 1) commit();              // sub-tile i-2
     if (i > 0) dq_mma();              // sub-tile i-1
     release();                        // sub-tile i-2
@@ -1063,7 +1190,7 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
       lds_barrier();
       role.seg_kd(sg);     // dQ waves: K columns from LDS
       lds_barrier();
-      role.seg_stage(sg);  // dQ waves: sub-tile 0 into LDS, load sub-tile 1
+      role.seg_stage(sg);  // dQ waves: sub-tile 0 has landed
       lds_barrier();
       const unsigned long long s1 = wclock();
       // (sg.n >= 1: the body runs at least once, which also tells the
