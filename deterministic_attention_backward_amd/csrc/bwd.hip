@@ -455,41 +455,39 @@ struct TileRole {
   // The exponent is one explicit fused multiply-add, so its rounding (and with
   // it every bit downstream) does not depend on how the compiler schedules
   // this code.
-  __device__ __forceinline__ void soft(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
-                                       f32x16& dp) {
+  // (as probs(): two paths for a causal mask, one for the others)
+  template <bool MASK>
+  __device__ __forceinline__ void soft_path(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
+                                            f32x16& dp) {
     const float* Ls = L.lse(buf);
     const float* Ds = L.dl(buf);
     const int key_g = kv_base + 32 * a + l32;
-    if (need_mask) {  // diagonal tile of a causal mask, or the ragged last KV tile
-      const bool key_ok = key_g < p.S;
+    const bool key_ok = key_g < p.S || !need_mask;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
-        const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
+      const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i = 4 * g + b;
+      for (int b = 0; b < 4; ++b) {
+        const int i = 4 * g + b;
+        float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
+        if constexpr (MASK) {
           const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
-          float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
-          const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
-          pv = vis ? pv : 0.0f;
-          s[i] = pv;
-          dp[i] = pv * (dp[i] - D4[b]);
+          pv = key_ok && (!CAUSAL || key_g <= q_g) ? pv : 0.0f;
         }
+        s[i] = pv;
+        dp[i] = pv * (dp[i] - D4[b]);
       }
+    }
+  }
+  // the mask applies on the diagonal tile of a causal mask and on the ragged last KV tile
+  __device__ __forceinline__ void soft(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
+                                       f32x16& dp) {
+    if constexpr (CAUSAL) {
+      if (need_mask) soft_path<true>(m, buf, q_base, kv_base, true, s, dp);
+      else soft_path<false>(m, buf, q_base, kv_base, false, s, dp);
     } else {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
-        const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i = 4 * g + b;
-          const float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
-          s[i] = pv;
-          dp[i] = pv * (dp[i] - D4[b]);
-        }
-      }
+      soft_path<true>(m, buf, q_base, kv_base, need_mask, s, dp);
     }
   }
 
@@ -544,26 +542,37 @@ struct TileRole {
   // the packed dS of row block 0 is carried over barrier X. The arithmetic of
   // every element is that of soft() and accumulate().
 
-  // P from S in place (soft()'s first half)
+  // P from S in place (soft()'s first half). A causal mask compiles a masked
+  // and an unmasked path (the mask test per score would cost every tile); the
+  // other masks test only the key (the ragged last KV tile), one path for all
+  // tiles, in which need_mask false lets every key pass.
   template <bool MASK>
-  __device__ __forceinline__ void probs(int m, int buf, int q_base, int kv_base, f32x16& sc) {
+  __device__ __forceinline__ void probs_path(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& sc) {
     const float* Ls = L.lse(buf) + 32 * m + 4 * hh;
     const int key_g = kv_base + 32 * a + l32;
-    const bool key_ok = key_g < p.S;
+    const bool key_ok = key_g < p.S || !need_mask;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const f32x4 L4 = *(const f32x4*)&Ls[8 * g];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int i = 4 * g + b;
-        float pv = fast_exp2(__builtin_fmaf(sc[i], p.scale_log2, -L4[b]));
+        const float pv = fast_exp2(__builtin_fmaf(sc[i], p.scale_log2, -L4[b]));
         if constexpr (MASK) {
           const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
-          const bool vis = key_ok && (!CAUSAL || key_g <= q_g);
-          pv = vis ? pv : 0.0f;
+          sc[i] = key_ok && (!CAUSAL || key_g <= q_g) ? pv : 0.0f;
+        } else {
+          sc[i] = pv;
         }
-        sc[i] = pv;
       }
+    }
+  }
+  __device__ __forceinline__ void probs(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& sc) {
+    if constexpr (CAUSAL) {
+      if (need_mask) probs_path<true>(m, buf, q_base, kv_base, true, sc);
+      else probs_path<false>(m, buf, q_base, kv_base, false, sc);
+    } else {
+      probs_path<true>(m, buf, q_base, kv_base, need_mask, sc);
     }
   }
 
@@ -633,8 +642,7 @@ struct TileRole {
                                               bf16x8& d1) {
     f32x16 sc, dpr;
     mma(m, buf, sc, dpr);
-    if (need_mask) probs<true>(m, buf, q_base, kv_base, sc);
-    else probs<false>(m, buf, q_base, kv_base, sc);
+    probs(m, buf, q_base, kv_base, need_mask, sc);
     dvalues(m, buf, sc, dpr, d0, d1);
   }
 
