@@ -1281,13 +1281,15 @@ __device__ __forceinline__ void fill_nan(bf16* x, long long n, long long t0, lon
 
 template <int D>
 __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, bf16* dk, bf16* dv,
-                                                       const int* header, long long BH, int S, int S_pad, int BR,
+                                                       const int* header, long long BH, int S, int S_pad,
                                                        int quad_major, float scale, long long kv_elems) {
-  // dq_ws holds, per query sub-tile of BR rows, 32 x 32 blocks in MFMA register
-  // order (see the dQ waves: quad-major or element-major within a block); one
-  // thread converts accumulators 4g..4g+3 of one lane: four consecutive rows
-  // of one feature column.
-  constexpr int ND = D / 32;
+  // dq_ws holds, per 32 query rows of a head, D / 32 blocks of 32 x 32 in MFMA
+  // register order (see the dQ waves: quad-major or element-major within a
+  // block), contiguous. A workgroup takes one such row block: each thread
+  // converts the accumulators 4g..4g+3 of one lane (four rows of one feature
+  // column) into an LDS tile, then writes whole rows, 16 bytes per thread.
+  constexpr int ND = D / 32, NQ = 32 * D / 4 / 256, NC = 32 * D / 8 / 256, TP = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 tile[32 * TP];
   const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long nthreads = (long long)gridDim.x * blockDim.x;
   if (call_failed(header)) {
@@ -1296,27 +1298,36 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
     fill_nan(dv, kv_elems, t0, nthreads);
     return;
   }
-  const long long n4 = BH * S_pad * (D / 4);
-  for (long long i = t0; i < n4; i += nthreads) {
-    const long long sub = i / (BR * D / 4);  // bh * (S_pad / BR) + sub-tile
-    const int r = (int)(i % (BR * D / 4));
-    const int blk = r >> 8, g = (r >> 6) & 3, lane = r & 63;
-    const int col = 32 * (blk % ND) + (lane & 31);
-    const int row0 = 32 * (blk / ND) + 8 * g + 4 * (lane >> 5);
-    const long long bh = sub / (S_pad / BR);
-    const int s0 = (int)(sub % (S_pad / BR)) * BR + row0;
-    f32x4 v;
-    if (quad_major) {
-      v = *(const f32x4*)(dq_ws + i * 4);
-    } else {
-      const float* b = dq_ws + (i - r) * 4 + blk * 1024 + 256 * g + lane;
+  const int rbh = S_pad / 32;  // row blocks per head
+  for (long long rb = blockIdx.x; rb < BH * rbh; rb += gridDim.x) {  // workgroup-uniform
+    const long long bh = rb / rbh;
+    const int r0 = (int)(rb - bh * rbh) * 32;
+    const float* src = dq_ws + (bh * S_pad + r0) * D;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) v[k] = b[64 * k];
+    for (int j = 0; j < NQ; ++j) {
+      const int q = threadIdx.x + 256 * j;  // f32x4 q of the row block: block q / 256, quad g, lane
+      const int blk = q >> 8, g = (q >> 6) & 3, lane = q & 63;
+      f32x4 v;
+      if (quad_major) {
+        v = *(const f32x4*)(src + 4 * q);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = src[blk * 1024 + (4 * g + k) * 64 + lane];
+      }
+      const int row = 8 * g + 4 * (lane >> 5), col = 32 * blk + (lane & 31);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tile[(row + k) * TP + col] = to_bf16(v[k] * scale);
     }
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (s0 + k < S) dq[(bh * S + s0 + k) * D + col] = to_bf16(v[k] * scale);
+    for (int j = 0; j < NC; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int row = c / (D / 8), part = c % (D / 8);
+      if (r0 + row < S) *(bf16x8*)(dq + (bh * S + r0 + row) * D + 8 * part) = *(const bf16x8*)&tile[row * TP + 8 * part];
+    }
+    __syncthreads();  // (the next row block reuses the tile)
   }
+  static_assert(ND * 32 == D && NQ * 256 * 4 == 32 * D && NC * 256 * 8 == 32 * D, "row block split");
 }
 
 // --------------------------------------------------------------------------------------
@@ -1430,6 +1441,7 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   pp.S_pad = a.S_pad;
   pp.n_flags = BH * a.lay.flag_stride;
   pp.dq_ws_elems = a.atomic ? BH * a.S_pad * a.D : 0;
+  if (a.S_pad % 32 != 0) return hipErrorInvalidValue;  // (S_pad = tiles x T; the post-pass takes 32 rows at a time)
   {
     const long long want = (pp.rows * (a.D / 8) + 255) / 256;
     const unsigned grid = (unsigned)(want < 4096 ? (want < 1 ? 1 : want) : 4096);
@@ -1490,17 +1502,16 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   }
 
   {
-    const long long want = (BH * a.S_pad * (a.D / 4) + 255) / 256;
-    const unsigned g = (unsigned)(want < 8192 ? (want < 1 ? 1 : want) : 8192);
+    const long long want = BH * (a.S_pad / 32);  // row blocks
+    const unsigned g = (unsigned)(want < 16384 ? (want < 1 ? 1 : want) : 16384);
     // (grouped heads: dk and dv are written by the group sum below, which checks the flag itself)
     const long long kv_elems = mp.group > 1 ? 0 : BH * a.S * a.D;
     if (a.D == 64)
       hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
-                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, a.BR, atomic ? 0 : 1, a.scale, kv_elems);
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 0 : 1, a.scale, kv_elems);
     else
       hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
-                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, a.BR, atomic ? 0 : 1, a.scale,
-                         kv_elems);
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 0 : 1, a.scale, kv_elems);
     e = hipGetLastError();
   }
   if (e == hipSuccess && mp.group > 1) {
