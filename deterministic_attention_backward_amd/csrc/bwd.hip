@@ -264,6 +264,7 @@ struct Geo {
   static_assert(QBW >= 1 && QBW * NB == MB * ND && QBW <= ND && ND % QBW == 0, "dQ block split");
   static_assert(PPW >= 1 && PIECES % NA == 0 && T % BR == 0 && BR % 64 == 0 && NA >= 2, "staging split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(V_LDS || T * DP * 2 <= RM_BYTES, "D = 64: V rows and staged dV fit a staging buffer");
 };
 
 template <class G>
@@ -735,9 +736,11 @@ struct TileRole {
     }
     // bf16 dK and dV through LDS: this wave's own 32 rows of the K-row region
     // (idle once the dQ waves have read K^T) take dK, and its rows of the
-    // V-row region (D = 128) or of a staging buffer (free between segments)
-    // take dV, written as the accumulators hold them (four features of one key
-    // per lane). Both are written first, which frees the accumulator
+    // V-row region (D = 128) or of staging buffer 1 (D = 64: the buffer its V
+    // rows came in through; idle until the next segment's second sub-tile,
+    // staged three barriers later, whereas the DMA of the next segment's first
+    // sub-tile into buffer 0 may already be in flight) take dV, written as the
+    // accumulators hold them (four features of one key per lane). Both are written first, which frees the accumulator
     // registers; then they are read back along the rows, so that each store
     // instruction writes whole rows (full cache lines) instead of a 16-byte
     // piece of 32 rows.
@@ -746,7 +749,7 @@ struct TileRole {
     int wofs = (32 * a + l32) * G::DP + 4 * hh, rofs = (32 * a + lane / (G::D / 8)) * G::DP + 8 * (lane % (G::D / 8));
     asm volatile("" : "+v"(wofs), "+v"(rofs));
     bf16* stg_k = L.kt();
-    bf16* stg_v = G::V_LDS ? L.v() : (bf16*)L.q(0);
+    bf16* stg_v = G::V_LDS ? L.v() : (bf16*)L.q(1);
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
 #pragma unroll
