@@ -2,8 +2,9 @@
 """Benchmark of the deterministic attention backward on one MI355X.
 
 One step = one call of the deterministic backward (pre-pass, main tile
-kernel with the ordered dQ reduction, and the post-pass that converts the
-fp32 dQ accumulator to bf16 dq), on synthetic bf16 inputs already resident
+kernel with the ordered dQ reduction, whose last contributor of each dQ
+sub-tile writes bf16 dq, and the post-pass that checks the call's failure
+flag), on synthetic bf16 inputs already resident
 in HBM. The headline workload is the causal B=4, H=32, S=4096, D=128 case;
 the same shape with a full mask is measured in the same run and carried as
 a sub-record of the line. Every deterministic schedule valid for the mask is

@@ -925,8 +925,14 @@ struct DqRole {
   int h_flag = 0, h_r = 0;
   bool h_last = true;
   float* h_row = nullptr;
+  bf16* h_dq = nullptr;  // the sub-tile's first row of dq
+  int h_rows = 0;        // its rows within the sequence
 
-  // The dQ accumulator is stored in the MFMA's own register order: per query
+  // The dQ products take their operands in the order (K columns, dS rows), so
+  // each 32 x 32 accumulator holds a block of dQ^T: lane l owns query row
+  // l mod 32 and, per register quad g, the four consecutive feature columns
+  // 8g + 4 (l / 32) + 0..3 (four bf16 of dq are one 8-byte piece of a row).
+  // The accumulator is stored in the MFMA's own register order: per query
   // sub-tile, 32 x 32 blocks (row block mb, feature block nb) of 1024 floats.
   // Every contributor of a block holds it in the same lanes, so
   //  - deterministic modes, "quad-major": accumulators 4g..4g+3 of lane l at
@@ -943,7 +949,7 @@ struct DqRole {
     for (int x = 0; x < QBW; ++x) {
       acc[x] = zero16();
 #pragma unroll
-      for (int c = 0; c < TC; ++c) acc[x] = mfma32(dsA[c], Kd[x][c], acc[x]);
+      for (int c = 0; c < TC; ++c) acc[x] = mfma32(Kd[x][c], dsA[c], acc[x]);
     }
   }
 
@@ -956,7 +962,10 @@ struct DqRole {
     h_flag = sg.bh * p.flag_stride + (t.q * NSUB + sg.half<NSUB>(j)) * G::NB + b;
     h_r = ATOMIC ? 0 : sched_rank(p.N, CAUSAL, p.sched, t.q, sg.kv);
     h_last = ATOMIC ? true : (h_r == sched_contributors(p.N, CAUSAL, t.q) - 1);
-    h_row = p.dq_ws + ((size_t)sg.bh * p.S_pad + t.q * G::T + sg.half<NSUB>(j) * BR) * D;  // uniform
+    const int q0 = t.q * G::T + sg.half<NSUB>(j) * BR;
+    h_row = p.dq_ws + ((size_t)sg.bh * p.S_pad + q0) * D;  // uniform
+    h_dq = p.dq + ((size_t)sg.bh * p.S + q0) * D;
+    h_rows = p.S - q0;
     if (ATOMIC || h_r == 0) return;
     // wait until the previous contributor's wave b has handed over (flag == r)
     const int target = h_r + (h_flag == p.poison_flag ? 0x40000000 : 0);
@@ -1003,6 +1012,30 @@ struct DqRole {
       }
       return;
     }
+    if (h_last) {
+      // The sub-tile's final sum: its last contributor writes dq = bf16(scale x
+      // sum) into dq itself (the conversion the post-pass does for the atomic
+      // variant), and no fp32 sum: quad g of block x is the 8-byte piece of
+      // row 32 mb + l32 at feature column 32 (nb0 + x) + 8g + 4hh.
+      // (one opaque per-lane base and constant offsets)
+      int lrow = 32 * mb + l32;
+      unsigned lofs = 2u * (unsigned)(lrow * D + 32 * nb0 + 4 * hh);
+      asm volatile("" : "+v"(lrow), "+v"(lofs));
+      if (lrow < h_rows) {
+#pragma unroll
+        for (int x = 0; x < QBW; ++x) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 b;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              b[k] = to_bf16((h_r > 0 ? prev[x][4 * g + k] + acc[x][4 * g + k] : acc[x][4 * g + k]) * p.scale);
+            *at_bytes((bf16x4*)h_dq, lofs + 2u * (unsigned)(32 * x + 8 * g)) = b;
+          }
+        }
+      }
+      return;
+    }
     if (XCD) {
       // (the first contributor stores its partial as it is)
 #pragma unroll
@@ -1031,10 +1064,8 @@ struct DqRole {
       }
     }
     asm volatile("" ::: "memory");
-    if (!h_last) {
-      pend = h_flag;
-      pend_val = h_r + 1;
-    }
+    pend = h_flag;  // (not the last contributor: the next one waits for this)
+    pend_val = h_r + 1;
   }
 
   // The hand-off of sub-tile j is spread over two intervals so that the
@@ -1285,12 +1316,15 @@ __device__ __forceinline__ void fill_nan(bf16* x, long long n, long long t0, lon
 template <int D>
 __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16* dq, bf16* dk, bf16* dv,
                                                        const int* header, long long BH, int S, int S_pad,
-                                                       int quad_major, float scale, long long kv_elems) {
-  // dq_ws holds, per 32 query rows of a head, D / 32 blocks of 32 x 32 in MFMA
-  // register order (see the dQ waves: quad-major or element-major within a
-  // block), contiguous. A workgroup takes one such row block: each thread
-  // converts the accumulators 4g..4g+3 of one lane (four rows of one feature
-  // column) into an LDS tile, then writes whole rows, 16 bytes per thread.
+                                                       int convert, float scale, long long kv_elems) {
+  // Fills dq, dk and dv with NaN if the main kernel gave up a wait. Else, for
+  // the atomic variant (convert != 0; the deterministic modes write dq in the
+  // main kernel), converts its sums: dq_ws holds, per 32 query rows of a
+  // head, D / 32 blocks of 32 x 32 in MFMA register order (element-major within
+  // a block, see the dQ waves), contiguous. A workgroup takes one such row
+  // block: each thread converts the accumulators 4g..4g+3 of one lane (four
+  // features of one row) into an LDS tile, then writes whole rows, 16 bytes
+  // per thread.
   constexpr int ND = D / 32, NQ = 32 * D / 4 / 256, NC = 32 * D / 8 / 256, TP = D + 8;
   __shared__ __attribute__((aligned(16))) bf16 tile[32 * TP];
   const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1301,6 +1335,7 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
     fill_nan(dv, kv_elems, t0, nthreads);
     return;
   }
+  if (!convert) return;  // (the deterministic modes: the main kernel wrote dq)
   const int rbh = S_pad / 32;  // row blocks per head
   for (long long rb = blockIdx.x; rb < BH * rbh; rb += gridDim.x) {  // workgroup-uniform
     const long long bh = rb / rbh;
@@ -1311,15 +1346,15 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(const float* dq_ws, bf16*
       const int q = threadIdx.x + 256 * j;  // f32x4 q of the row block: block q / 256, quad g, lane
       const int blk = q >> 8, g = (q >> 6) & 3, lane = q & 63;
       f32x4 v;
-      if (quad_major) {
-        v = *(const f32x4*)(src + 4 * q);
-      } else {
+      // (element-major: the atomic variant's layout)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = src[blk * 1024 + (4 * g + k) * 64 + lane];
-      }
-      const int row = 8 * g + 4 * (lane >> 5), col = 32 * blk + (lane & 31);
+      for (int k = 0; k < 4; ++k) v[k] = src[blk * 1024 + (4 * g + k) * 64 + lane];
+      // (blocks of dQ^T: lane l holds row l mod 32, features 8g + 4 (l / 32) + 0..3)
+      const int row = lane & 31, col = 32 * blk + 8 * g + 4 * (lane >> 5);
+      bf16x4 b;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) tile[(row + k) * TP + col] = to_bf16(v[k] * scale);
+      for (int k = 0; k < 4; ++k) b[k] = to_bf16(v[k] * scale);
+      *(bf16x4*)&tile[row * TP + col] = b;
     }
     __syncthreads();
 #pragma unroll
@@ -1505,16 +1540,17 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   }
 
   {
-    const long long want = BH * (a.S_pad / 32);  // row blocks
+    // (deterministic modes: a check of the failure flag, and the NaN fill if set)
+    const long long want = atomic ? BH * (a.S_pad / 32) : 1024;  // row blocks
     const unsigned g = (unsigned)(want < 16384 ? (want < 1 ? 1 : want) : 16384);
     // (grouped heads: dk and dv are written by the group sum below, which checks the flag itself)
     const long long kv_elems = mp.group > 1 ? 0 : BH * a.S * a.D;
     if (a.D == 64)
       hipLaunchKernelGGL(bwd_post_kernel<64>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
-                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 0 : 1, a.scale, kv_elems);
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 1 : 0, a.scale, kv_elems);
     else
       hipLaunchKernelGGL(bwd_post_kernel<128>, dim3(g), dim3(256), 0, stream, dq_ws, (bf16*)a.dq, (bf16*)a.dk,
-                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 0 : 1, a.scale, kv_elems);
+                         (bf16*)a.dv, (const int*)header, BH, a.S, a.S_pad, atomic ? 1 : 0, a.scale, kv_elems);
     e = hipGetLastError();
   }
   if (e == hipSuccess && mp.group > 1) {
