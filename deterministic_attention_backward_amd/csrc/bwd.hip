@@ -13,8 +13,9 @@
 // schedule fixes, accumulates dK_j/dV_j in MFMA accumulators and, per query
 // sub-tile, hands its dQ partial to the fp32 dQ workspace in the schedule's
 // order: wait until the sub-tile's counter equals r(i, j), add, then (one
-// sub-tile later, when the adds have long completed) increment the counter. A
-// post-pass converts the fp32 accumulator to bf16 dq.
+// sub-tile later, when the adds have long completed) increment the counter.
+// The last contributor of a sub-tile writes bf16 dq itself; a post-pass
+// checks the call's failure flag (and converts the atomic variant's sums).
 #include "../../include/attn_det.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -914,13 +915,14 @@ struct DqRole {
   // compiler needs no wait of its own before the loop's LDS reads.)
   __device__ __forceinline__ void seg_stage(const Seg&) { stage_wait(); }
 
-  // The hand-off of sub-tile j runs in three steps spread over the next
-  // interval so that its memory latencies overlap other work:
-  //   acquire (before barrier X): dQ = dS K into registers; wait for the turn;
-  //            start the loads of the running sum;
-  //   commit  (after barrier X):  add and store (or the atomic RMWs);
-  //   release (next interval):    once the stores have completed, count this
-  //            wave's contribution on the sub-tile's counter.
+  // The hand-off of sub-tile j runs in three steps (part1 and part2 below say
+  // in which intervals):
+  //   acquire: where the partial goes; wait for the turn; start the loads of
+  //            the running sum;
+  //   commit:  add and store (or the atomic RMWs; the last contributor writes
+  //            bf16 dq instead);
+  //   release: once the stores have completed, hand over to the next
+  //            contributor (write its value into this wave's flag).
   f32x16 acc[QBW], prev[QBW];
   int h_flag = 0, h_r = 0;
   bool h_last = true;
@@ -1296,7 +1298,7 @@ __global__ void __launch_bounds__(T / 16 * 64) bwd_main_kernel(MainParams p) {
 }
 
 // --------------------------------------------------------------------------------------
-// post-pass: dq = bf16(scale * dQ accumulator)
+// post-pass: the failure check; for the atomic variant dq = bf16(scale * dQ accumulator)
 
 // A tripped wait bound (header[1], set by the main kernel) makes the call's
 // results unusable: the dQ order may have been broken. The passes after the
