@@ -798,6 +798,12 @@ struct DqRole {
   int tb, lane, b, l32, hh, mb, nb0;
   bf16x8 Kd[QBW][TC];   // B operand of dQ: this wave's feature columns, all keys of the tile
   bf16x8 dsA[TC];       // A operand of dQ: dS rows of this wave's row block
+  // Full-mask Shift with the XCD-local hand-off: the running sums of a
+  // sub-tile are loaded in the next interval's part1, after the staging DMA
+  // (which then no longer queues behind them); where contributors wait on
+  // each other's turns (the other schedules, the causal mask, the device-wide
+  // hand-off) the loads go right after the turn, as early as they can.
+  bool late_loads = false;
   int pend = -1;      // flag this wave still owes a hand-over on
   int pend_val = 0;   // the value it will write there
   WaitClock* wc = nullptr;  // profiling build only
@@ -811,6 +817,7 @@ struct DqRole {
     constexpr int per_row = G::ND / QBW;
     mb = b / per_row;
     nb0 = QBW * (b % per_row);
+    late_loads = XCD && !CAUSAL && p.sched == SCHED_SHIFT;
   }
 
   // LDS DMA of query rows q0 .. q0 + BR - 1 of head bh into staging buffer
@@ -990,6 +997,12 @@ struct DqRole {
       seen = flag_read(fl);
     }
     if constexpr (kProfileWait) wc->turn += wclock() - w0;
+    if (!late_loads) load_sums();
+  }
+  // start the loads of the acquired sub-tile's running sum (none for its first
+  // contributor or the atomic variant)
+  __device__ __forceinline__ void load_sums() {
+    if (ATOMIC || h_r == 0) return;
     // XCD-local: every contributor of this tile runs on this XCD, so its L2
     // holds the accumulator coherently for all of them: read the running sum
     // there. Across XCDs: read it from the device-wide coherence point.
@@ -1089,6 +1102,7 @@ struct DqRole {
   __device__ __forceinline__ void part1(const Seg& sg, int i) {
     if (i > 0) read_ds();
     if (i + 1 < sg.n) stage(sg.bh, sub_row0(sg, i + 1), (i + 1) & 1);
+    if (late_loads && i > 1) load_sums();  // sub-tile i-2, acquired in the previous part2
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
@@ -1106,10 +1120,14 @@ struct DqRole {
 
   __device__ __forceinline__ void seg_end(const Seg& sg) {
     read_ds();                        // dS of the last sub-tile
-    if (sg.n > 1) commit();           // sub-tile n-2
+    if (sg.n > 1) {
+      if (late_loads) load_sums();
+      commit();                       // sub-tile n-2
+    }
     dq_mma();                         // sub-tile n-1
     release();
     acquire(sg, sg.n - 1);
+    if (late_loads) load_sums();
     commit();
     release();
   }
