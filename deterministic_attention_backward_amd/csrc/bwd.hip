@@ -308,20 +308,10 @@ struct Seg {
 
 // ---- tile waves
 
-#ifndef ATTN_TILE_PIPE
-#define ATTN_TILE_PIPE 1
-#endif
-#ifndef ATTN_TILE_ILV
-#define ATTN_TILE_ILV 1
-#endif
 
 template <class G, bool CAUSAL, int MODE>
 struct TileRole {
   static constexpr int KC = G::KC, ND = G::ND, MB = G::MB, NSUB = G::NSUB;
-  // software-pipelined row blocks (D = 64: registers to spare for a second S/dP block)
-  static constexpr bool PIPE = ATTN_TILE_PIPE != 0 && G::D == 64;
-  // D = 128: dS computed between the dV MFMAs (see probs .. dkeys)
-  static constexpr bool ILV = ATTN_TILE_ILV != 0 && !PIPE && G::ND == 4;
   const MainParams& p;
   Lds<G> L;
   int tid, lane, a, l32, hh;
@@ -332,8 +322,7 @@ struct TileRole {
   static constexpr bool VL = G::V_LDS;
   bf16x8 Kr[KC], Vr[VL ? 1 : KC];
   f32x16 dKa[ND], dVa[ND];
-  f32x16 s, dp;  // first row block of the current sub-tile, carried over barrier X
-  bf16x8 dsb[2];  // (D = 128 order: only its dS, packed, is carried over X)
+  bf16x8 dsb[2];  // dS of the current sub-tile's first row block, packed, carried over barrier X
   WaitClock* wc = nullptr;  // profiling build only
 
   __device__ __forceinline__ TileRole(const MainParams& p_, Lds<G> L_) : p(p_), L(L_) {
@@ -416,12 +405,6 @@ struct TileRole {
   __device__ __forceinline__ void seg_kd(const Seg&) {}
   __device__ __forceinline__ void seg_stage(const Seg&) {}
 
-  // S and dP of row block m, turned into P and dS in place
-  __device__ __forceinline__ void sdp(int m, int buf, int q_base, int kv_base, bool need_mask) {
-    mma(m, buf, s, dp);
-    soft(m, buf, q_base, kv_base, need_mask, s, dp);
-  }
-
   // S and dP of row block m (raw scores)
   __device__ __forceinline__ void mma(int m, int buf, f32x16& s, f32x16& dp) {
     // (the lane constants are re-read here so that the compiler computes the
@@ -449,105 +432,28 @@ struct TileRole {
       }
       s = mfma32(qa[c & 1], Kr[c], s);
       dp = mfma32(oa[c & 1], VL ? vb[c & 1] : Vr[VL ? 0 : c], dp);
-      if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // P = exp2(S scale log2(e) - LSE log2(e)) and dS = P (dP - Delta), in place.
-  // The exponent is one explicit fused multiply-add, so its rounding (and with
-  // it every bit downstream) does not depend on how the compiler schedules
-  // this code.
-  // (as probs(): two paths for a causal mask, one for the others)
-  template <bool MASK>
-  __device__ __forceinline__ void soft_path(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
-                                            f32x16& dp) {
-    const float* Ls = L.lse(buf);
-    const float* Ds = L.dl(buf);
-    const int key_g = kv_base + 32 * a + l32;
-    const bool key_ok = key_g < p.S || !need_mask;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 L4 = *(const f32x4*)&Ls[32 * m + 8 * g + 4 * hh];
-      const f32x4 D4 = *(const f32x4*)&Ds[32 * m + 8 * g + 4 * hh];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int i = 4 * g + b;
-        float pv = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -L4[b]));
-        if constexpr (MASK) {
-          const int q_g = q_base + 32 * m + 8 * g + 4 * hh + b;
-          pv = key_ok && (!CAUSAL || key_g <= q_g) ? pv : 0.0f;
-        }
-        s[i] = pv;
-        dp[i] = pv * (dp[i] - D4[b]);
-      }
-    }
-  }
-  // the mask applies on the diagonal tile of a causal mask and on the ragged last KV tile
-  __device__ __forceinline__ void soft(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& s,
-                                       f32x16& dp) {
-    if constexpr (CAUSAL) {
-      if (need_mask) soft_path<true>(m, buf, q_base, kv_base, true, s, dp);
-      else soft_path<false>(m, buf, q_base, kv_base, false, s, dp);
-    } else {
-      soft_path<true>(m, buf, q_base, kv_base, need_mask, s, dp);
-    }
-  }
+  // Row block m: S and dP (their MFMAs interleaved, mma()), then P in place;
+  // then dV^T += dO^T P with dS = P (dP - Delta) computed between those MFMAs
+  // (16 / ND scores per feature block), so that this vector work runs while
+  // they do; then dS^T to LDS and dK^T += Q^T dS. Only the packed dS of row
+  // block 0 is carried over barrier X. The dV and dK products take the
+  // staged dO and Q rows through the transposing read as their A operands
+  // (trB: 8 queries in the order of the C-matrix rows the lane holds, 4 hh +
+  // 0..3 and 8 + 4 hh + 0..3) and P or dS, packed, as their B operands, so the
+  // accumulators hold dV^T and dK^T blocks: a lane owns four consecutive
+  // features of one key per register quad.
 
-  // dS^T of row block m to LDS; dV += P^T dO and dK += dS^T Q. B operand of
-  // feature block n, query half h2 of row block m (trB): 8 queries in the
-  // order of the C-matrix rows the lane holds (4 hh + 0..3, 8 + 4 hh + 0..3)
-
-  __device__ __forceinline__ void accumulate(int m, int buf) {
-    accumulate(m, buf, pack8(s, 0), pack8(s, 8), pack8(dp, 0), pack8(dp, 8));
-  }
-  __device__ __forceinline__ void accumulate(int m, int buf, bf16x8 pb0, bf16x8 pb1, bf16x8 db0, bf16x8 db1) {
-    bf16* drow = &L.dst()[(32 * a + l32) * G::SP + 32 * m + 4 * hh];  // four consecutive queries per write
-    *(bf16x4*)(drow + 0) = __builtin_shufflevector(db0, db0, 0, 1, 2, 3);
-    *(bf16x4*)(drow + 8) = __builtin_shufflevector(db0, db0, 4, 5, 6, 7);
-    *(bf16x4*)(drow + 16) = __builtin_shufflevector(db1, db1, 0, 1, 2, 3);
-    *(bf16x4*)(drow + 24) = __builtin_shufflevector(db1, db1, 4, 5, 6, 7);
-    int tb[2] = {tl.base[0], tl.base[1]}, th = tl.hi;
-    asm volatile("" : "+v"(tb[0]), "+v"(tb[1]), "+v"(th));
-    const char* QB = L.q(buf) + 32 * m * G::RB;
-    const char* OB = L.o(buf) + 32 * m * G::RB;
-    bf16x8 ov[2][2], qv[2][2];  // B operands one feature block ahead
-    {
-      const int nx = th << 6;
-      ov[0][0] = trB<G::RB>(OB, 0, tb, nx);
-      ov[0][1] = trB<G::RB>(OB, 1, tb, nx);
-      qv[0][0] = trB<G::RB>(QB, 0, tb, nx);
-      qv[0][1] = trB<G::RB>(QB, 1, tb, nx);
-    }
-#pragma unroll
-    for (int n = 0; n < ND; ++n) {
-      if (n + 1 < ND) {
-        const int nx = ((n + 1) ^ th) << 6;
-        ov[(n + 1) & 1][0] = trB<G::RB>(OB, 0, tb, nx);
-        ov[(n + 1) & 1][1] = trB<G::RB>(OB, 1, tb, nx);
-        qv[(n + 1) & 1][0] = trB<G::RB>(QB, 0, tb, nx);
-        qv[(n + 1) & 1][1] = trB<G::RB>(QB, 1, tb, nx);
-      }
-      // dO^T P and Q^T dS: the accumulators hold dV^T and dK^T blocks, so a
-      // lane owns four consecutive features of one key per register quad
-      dVa[n] = mfma32(ov[n & 1][0], pb0, dVa[n]);
-      dVa[n] = mfma32(ov[n & 1][1], pb1, dVa[n]);
-      dKa[n] = mfma32(qv[n & 1][0], db0, dKa[n]);
-      dKa[n] = mfma32(qv[n & 1][1], db1, dKa[n]);
-      if constexpr (!PIPE) __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- D = 128 order. Row block m: S and dP (their MFMAs interleaved, as
-  // in mma()), then P in place; then dV^T += dO^T P with dS = P (dP - Delta)
-  // computed between those MFMAs (four scores per feature block), so that this
-  // vector work runs while they do; then dS^T to LDS and dK^T += Q^T dS. Only
-  // the packed dS of row block 0 is carried over barrier X. The arithmetic of
-  // every element is that of soft() and accumulate().
-
-  // P from S in place (soft()'s first half). A causal mask compiles a masked
-  // and an unmasked path (the mask test per score would cost every tile); the
-  // other masks test only the key (the ragged last KV tile), one path for all
-  // tiles, in which need_mask false lets every key pass.
+  // P = exp2(S scale log2(e) - LSE log2(e)) in place. The exponent is one
+  // explicit fused multiply-add, so its rounding (and with it every bit
+  // downstream) does not depend on how the compiler schedules this code. A
+  // causal mask compiles a masked and an unmasked path (the mask test per
+  // score would cost every tile); the other masks test only the key (the
+  // ragged last KV tile), one path for all tiles, in which need_mask false
+  // lets every key pass.
   template <bool MASK>
   __device__ __forceinline__ void probs_path(int m, int buf, int q_base, int kv_base, bool need_mask, f32x16& sc) {
     const float* Ls = L.lse(buf) + 32 * m + 4 * hh;
@@ -590,21 +496,29 @@ struct TileRole {
       ov[0][0] = trB<G::RB>(OB, 0, tb, nx);
       ov[0][1] = trB<G::RB>(OB, 1, tb, nx);
     }
-    f32x4 D4[2];
-    D4[0] = *(const f32x4*)&Ds[0];
+    // Delta of the four row quads: one quad ahead at D = 128 (one quad per
+    // feature block), all four at once at D = 64 (two per feature block)
+    constexpr int QN = 4 / ND;
+    f32x4 D4[4];
+#pragma unroll
+    for (int g = 0; g < (ND == 4 ? 1 : 4); ++g) D4[g] = *(const f32x4*)&Ds[8 * g];
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
       if (n + 1 < ND) {
         const int nx = ((n + 1) ^ th) << 6;
         ov[(n + 1) & 1][0] = trB<G::RB>(OB, 0, tb, nx);
         ov[(n + 1) & 1][1] = trB<G::RB>(OB, 1, tb, nx);
-        D4[(n + 1) & 1] = *(const f32x4*)&Ds[8 * (n + 1)];
+        if constexpr (ND == 4) D4[n + 1] = *(const f32x4*)&Ds[8 * (n + 1)];
       }
       dVa[n] = mfma32(ov[n & 1][0], pb0, dVa[n]);
       dVa[n] = mfma32(ov[n & 1][1], pb1, dVa[n]);
-      // dS of quad n of the block's rows
+      // dS of row quads QN n .. QN n + QN - 1 of the block
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dpr[4 * n + b] = sc[4 * n + b] * (dpr[4 * n + b] - D4[n & 1][b]);
+      for (int q = 0; q < QN; ++q) {
+        const int g = QN * n + q;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) dpr[4 * g + b] = sc[4 * g + b] * (dpr[4 * g + b] - D4[g][b]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     d0 = pack8(dpr, 0);
@@ -659,53 +573,21 @@ struct TileRole {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    if constexpr (ILV) {
-      block_front(0, i & 1, q_base, kv_base, need_mask, dsb[0], dsb[1]);
-    } else {
-      sdp(0, i & 1, q_base, kv_base, need_mask);
-    }
+    block_front(0, i & 1, q_base, kv_base, need_mask, dsb[0], dsb[1]);
   }
 
   __device__ __forceinline__ void part2(const Seg& sg, int i) {
     int q_base, kv_base;
     bool need_mask;
     where(sg, i, q_base, kv_base, need_mask);
-    if constexpr (ILV) {
-      // (row block 0's dS is written only now: the dQ waves read the previous
-      // sub-tile's before barrier X)
-      dkeys(0, i & 1, dsb[0], dsb[1]);
+    // (row block 0's dS is written only now: the dQ waves read the previous
+    // sub-tile's before barrier X)
+    dkeys(0, i & 1, dsb[0], dsb[1]);
 #pragma unroll
-      for (int m = 1; m < MB; ++m) {
-        bf16x8 d0, d1;
-        block_front(m, i & 1, q_base, kv_base, need_mask, d0, d1);
-        dkeys(m, i & 1, d0, d1);
-      }
-    } else if constexpr (PIPE) {
-      // row block m+1's scores are issued before row block m's dV/dK
-      // products, and its softmax follows them: with no scheduling fences the
-      // compiler can interleave one block's VALU work with the other's MFMAs
-      // (a finished block is kept packed to bf16, as the MFMAs take it)
-      bf16x8 pk[4] = {pack8(s, 0), pack8(s, 8), pack8(dp, 0), pack8(dp, 8)};
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        f32x16 sn, dn;
-        if (m + 1 < MB) mma(m + 1, i & 1, sn, dn);
-        accumulate(m, i & 1, pk[0], pk[1], pk[2], pk[3]);
-        if (m + 1 < MB) {
-          soft(m + 1, i & 1, q_base, kv_base, need_mask, sn, dn);
-          pk[0] = pack8(sn, 0);
-          pk[1] = pack8(sn, 8);
-          pk[2] = pack8(dn, 0);
-          pk[3] = pack8(dn, 8);
-        }
-      }
-    } else {
-      accumulate(0, i & 1);
-#pragma unroll
-      for (int m = 1; m < MB; ++m) {
-        sdp(m, i & 1, q_base, kv_base, need_mask);
-        accumulate(m, i & 1);
-      }
+    for (int m = 1; m < MB; ++m) {
+      bf16x8 d0, d1;
+      block_front(m, i & 1, q_base, kv_base, need_mask, d0, d1);
+      dkeys(m, i & 1, d0, d1);
     }
   }
 
