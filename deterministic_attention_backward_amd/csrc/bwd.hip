@@ -133,6 +133,7 @@ struct MainParams {
   bf16* dq;
   int *flags, *header, *heads;
   int S, S_pad, N, n_qsub, n_workers, n_units, sched, BH;
+  int ilv;  // heads whose workers share each run of XCD-queue tickets (1: one head after another)
   int H, group;  // query heads per batch; query heads per K/V head
   float* dkv;    // group > 1: per query head fp32 dK (scaled), then dV, [BH][S_pad][D] each
   int flag_stride, heads_row;  // int32 elements per head of flags / per queue row of heads
@@ -1022,9 +1023,42 @@ struct DqRole {
 #endif
 constexpr bool PASSES = ATTN_SUBTILE_PASSES != 0;
 
+#ifndef ATTN_HEAD_INTERLEAVE
+#define ATTN_HEAD_INTERLEAVE 0  // 0: by the rule below; otherwise that many heads
+#endif
+
+// Heads interleaved in an XCD queue for naive and Descending: 4, 2 or 1, the
+// most that keeps heads x workers within 256 on a causal mask and within 64
+// on a full one. (Interleaved runs on the 4k and 8k causal and the 2k, 4k and
+// 16k full shapes: more heads at once fill the gaps of the serial dQ chains;
+// past that bound the running sums of the heads in flight no longer stay in
+// the XCD's L2 between contributors, and the 16k full mask slows down.)
+inline int head_interleave(bool causal, int n_workers) {
+  if (ATTN_HEAD_INTERLEAVE > 0) return ATTN_HEAD_INTERLEAVE;
+  const int cap = causal ? 256 : 64;
+  int g = 4;
+  while (g > 1 && g * n_workers > cap) g /= 2;
+  return g;
+}
+
 #ifndef ATTN_ATOMIC_XCD_QUEUE
 #define ATTN_ATOMIC_XCD_QUEUE 1
 #endif
+
+// A head slot of an XCD queue once its run's first ticket has published it
+// (p.BH, and the call marked failed, if the wait bound runs out first).
+__device__ __forceinline__ int wait_slot(const MainParams& p, int* slot) {
+  int v;
+  uint32_t it = 0;
+  while ((v = l2_load(slot)) < 0) {
+    if (++it >= p.wait_limit) {
+      note_timeout(p.header);
+      return p.BH;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return v;
+}
 
 template <class G, bool CAUSAL, int MODE, class Role>
 __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, Role& role) {
@@ -1052,38 +1086,42 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
         sUnit[0] = u < p.n_units ? u / p.n_workers : p.BH;
         sUnit[1] = u % p.n_workers;
       } else {
-        // Units of one head are consecutive tickets of one XCD's queue; the
-        // ticket of a head's first worker claims the next unclaimed head (an
-        // atomic shared by all XCDs) and publishes it for the others through
-        // this XCD's L2 (lower tickets are held by running workgroups, so the
-        // wait below always ends).
+        // Units of one head are consecutive tickets of one XCD's queue or,
+        // with ilv > 1, ilv heads take turns within each run of ilv x workers
+        // tickets (worker 0 of each, then worker 1 of each, ...): where a
+        // worker waits only on the workers before it (naive, Descending),
+        // workgroups freed together then start on several heads at once
+        // instead of lining up behind one head's hand-offs. The first ticket
+        // of a run claims the run's ilv heads (an atomic shared by all XCDs)
+        // once the queue's previous run has claimed, so the heads of a queue
+        // only grow along it, and publishes the first of them through this
+        // XCD's L2 for the run's other tickets. Each wait here is for a lower
+        // ticket of the same queue, held by a running workgroup that
+        // publishes right after its atomic, so it ends. A ticket whose slot
+        // lies past the last head takes another ticket; a run that starts
+        // past it ends the queue for every later ticket as well.
         const int k = atomicAdd(&p.header[16 + xq], 1);
-        const int i = k / p.n_workers, wk = k % p.n_workers;
-        int head = p.BH;
-        if (i < p.BH) {
-          int* slot = &p.heads[xq * p.heads_row + i];
-          if (wk == 0) {
-            head = min(atomicAdd(&p.header[2], 1), p.BH);
-            l2_store(slot, head);
+        const int span = p.ilv * p.n_workers, grp = k / span, rem = k - grp * span;
+        const int wk = rem / p.ilv;
+        int first = p.BH;  // the run's first head
+        if (grp < p.BH) {
+          int* slot = &p.heads[xq * p.heads_row + grp];
+          if (rem == 0) {
+            if (grp == 0 || wait_slot(p, slot - 1) < p.BH) first = min(atomicAdd(&p.header[2], p.ilv), p.BH);
+            l2_store(slot, first);
           } else {
-            uint32_t it = 0;
-            while ((head = l2_load(slot)) < 0) {
-              if (++it >= p.wait_limit) {
-                note_timeout(p.header);
-                head = p.BH;
-                break;
-              }
-              __builtin_amdgcn_s_sleep(2);
-            }
+            first = wait_slot(p, slot);
           }
         }
-        sUnit[0] = head;
+        const int head = first + rem % p.ilv;
+        sUnit[0] = first >= p.BH ? p.BH : (head >= p.BH ? -1 : head);
         sUnit[1] = wk;
       }
     }
     lds_barrier();
     if constexpr (kProfileWait) wclk.claim += wclock() - c0;
     const int bh = __builtin_amdgcn_readfirstlane(sUnit[0]);
+    if (bh < 0) continue;  // a slot past the last head: take another ticket
     // Causal Shift: dQ tile i receives KV tiles i, i-1, ..., 0 in that order,
     // so worker j waits on worker j+1 at every step. Dealing a head's workers
     // last KV tile first starts every predecessor before its successor; in
@@ -1421,6 +1459,7 @@ hipError_t launch_bwd(const BwdArgs& a, int num_cu, hipStream_t stream) {
   mp.sched = a.atomic ? SCHED_NAIVE : a.sched;
   mp.n_workers = sched_workers(a.N, mp.sched);
   mp.n_units = (int)(BH * mp.n_workers);
+  mp.ilv = (!a.atomic && (mp.sched == SCHED_NAIVE || mp.sched == SCHED_DESCENDING)) ? head_interleave(a.causal != 0, mp.n_workers) : 1;
   mp.scale = a.scale;
   mp.scale_log2 = a.scale * 1.4426950408889634f;
   mp.wait_limit = a.wait_limit;

@@ -129,6 +129,34 @@ def test_backward_parity(case, protocol):
         dab.set_dq_protocol("auto")
 
 
+# Grids smaller than 8 x the workers of a head, so that some XCD queues have a
+# single workgroup, and head counts that leave the last run of interleaved
+# heads (naive, Descending) partial: every unit must still run exactly once,
+# whichever queue claims which heads first.
+SMALL_GRID = [
+    (1, 5, 300, 64, False, 41),   # 3 workers per head, 15 units: runs of 4 heads, the last one partial
+    (1, 5, 300, 64, True, 42),
+    (1, 7, 200, 128, True, 43),   # 2 workers per head, 14 units
+    (2, 3, 130, 128, False, 44),  # 2 workers per head, 12 units
+]
+
+
+@pytest.mark.parametrize("case", SMALL_GRID, ids=lambda c: "B%dH%dS%dD%d%s" % (c[0], c[1], c[2], c[3],
+                                                                                "c" if c[4] else "f"))
+def test_small_grids_run_every_unit(case):
+    B, H, S, D, causal, seed = case
+    c = Case(B, H, S, D, causal, seed)
+    dq_r, dk_r, dv_r = c.ref()
+    for sched in ("naive", "descending"):
+        say(f"small grid {case} schedule={sched}")
+        first = c.run(sched)
+        for name, g, r in (("dQ", first[0], dq_r), ("dK", first[1], dk_r), ("dV", first[2], dv_r)):
+            assert_close(f"{sched} {name}", f64(g), r)
+        for _ in range(5):  # (which queue claims which heads differs from call to call)
+            again = c.run(sched)
+            assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(first, again))
+
+
 DET_CASES = [
     (2, 4, 1024, 128, False, 31),
     (2, 4, 1024, 128, True, 32),
