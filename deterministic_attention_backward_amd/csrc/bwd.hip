@@ -1072,14 +1072,26 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
     xq = (int)(x & (kMaxQueues - 1));
   }
+  // The unit a workgroup runs next: [0] head, [1] worker, [2] how many units
+  // thread 0 has published (LDS starts undefined).
   int* sUnit = L.unit();
+  if (threadIdx.x == 0) sUnit[2] = 0;
+  lds_barrier();
+  int seq = 0;
   WaitClock wclk;
   if constexpr (kProfileWait) role.wc = &wclk;
   const unsigned long long t_start = wclock();
   unsigned long long n_sub = 0;
   for (;;) {
     const unsigned long long c0 = wclock();
-    lds_barrier();
+    ++seq;
+    // Thread 0 claims the next unit as soon as its own wave has finished the
+    // previous one and publishes it through LDS; the other waves wait only
+    // for that word, not at a barrier, so the tile waves claim and load the
+    // next K/V tile while the dQ waves still hand the last sub-tile over
+    // (they meet at the segment's first barrier). One slot suffices: thread 0
+    // reaches the next claim only after the segment's barriers, which every
+    // wave passes after reading this unit.
     if (threadIdx.x == 0) {
       if (!XCD) {
         const int u = atomicAdd(&p.header[0], 1);
@@ -1100,28 +1112,33 @@ __device__ __forceinline__ void run_units(const MainParams& p, const Lds<G>& L, 
         // publishes right after its atomic, so it ends. A ticket whose slot
         // lies past the last head takes another ticket; a run that starts
         // past it ends the queue for every later ticket as well.
-        const int k = atomicAdd(&p.header[16 + xq], 1);
-        const int span = p.ilv * p.n_workers, grp = k / span, rem = k - grp * span;
-        const int wk = rem / p.ilv;
-        int first = p.BH;  // the run's first head
-        if (grp < p.BH) {
-          int* slot = &p.heads[xq * p.heads_row + grp];
-          if (rem == 0) {
-            if (grp == 0 || wait_slot(p, slot - 1) < p.BH) first = min(atomicAdd(&p.header[2], p.ilv), p.BH);
-            l2_store(slot, first);
-          } else {
-            first = wait_slot(p, slot);
+        int head, wk;
+        for (;;) {
+          const int k = atomicAdd(&p.header[16 + xq], 1);
+          const int span = p.ilv * p.n_workers, grp = k / span, rem = k - grp * span;
+          wk = rem / p.ilv;
+          int first = p.BH;  // the run's first head
+          if (grp < p.BH) {
+            int* slot = &p.heads[xq * p.heads_row + grp];
+            if (rem == 0) {
+              if (grp == 0 || wait_slot(p, slot - 1) < p.BH) first = min(atomicAdd(&p.header[2], p.ilv), p.BH);
+              l2_store(slot, first);
+            } else {
+              first = wait_slot(p, slot);
+            }
           }
+          head = first >= p.BH ? p.BH : first + rem % p.ilv;
+          if (head < p.BH || first >= p.BH) break;  // a unit, or the end of the queue
         }
-        const int head = first + rem % p.ilv;
-        sUnit[0] = first >= p.BH ? p.BH : (head >= p.BH ? -1 : head);
+        sUnit[0] = head;
         sUnit[1] = wk;
       }
+      __hip_atomic_store(&sUnit[2], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    lds_barrier();
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sUnit[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) != seq)
+      __builtin_amdgcn_s_sleep(1);
     if constexpr (kProfileWait) wclk.claim += wclock() - c0;
     const int bh = __builtin_amdgcn_readfirstlane(sUnit[0]);
-    if (bh < 0) continue;  // a slot past the last head: take another ticket
     // Causal Shift: dQ tile i receives KV tiles i, i-1, ..., 0 in that order,
     // so worker j waits on worker j+1 at every step. Dealing a head's workers
     // last KV tile first starts every predecessor before its successor; in
