@@ -5,7 +5,8 @@ in [1, 700] (so tile counts odd and even, ragged tails of every size), one
 to four heads, one or two batches, both head sizes, both masks, every tile
 request, and grouped K/V heads. Each backward of every deterministic
 schedule and of the atomic variant is compared element by element with the
-float64 oracle on the HIP forward's O and LSE, to the same bar as
+float64 oracle on the HIP forward's O and LSE (which are checked against
+the oracle forward first), to the same bar as
 test_gpu_parity.py (grouped dK/dV: the widened per-element bound of
 test_gpu_gqa.py). The shapes come from a fixed seed, so a failure names a
 shape that reproduces.
@@ -80,6 +81,10 @@ def test_random_shape_parity(case):
     o, lse = dab.fwd(q, k, v, causal)
     torch.cuda.synchronize()
     scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = A.forward(f64(q), f64(k), f64(v), causal, scale)
+    mx, rel = A.compare(f64(o), o_ref)
+    assert mx <= TOL_ABS and rel <= TOL_REL, f"{case} forward O: max_abs={mx:.3e} rel_l2={rel:.3e}"
+    assert np.abs(f64(lse) - lse_ref).max() <= 1e-3, f"{case} forward LSE"
     ref = A.backward(f64(q), f64(k), f64(v), f64(o), f64(do), f64(lse), causal, scale)
     for sched in _schedules(S, D, causal, tile):
         say(f"  schedule={sched or 'atomic'}")
