@@ -15,7 +15,8 @@ Contents:
     Lemma 1 depth monotonicity and deadlock freedom.
   * ``makespan`` - that DAG run for many heads on a fixed number of
     processors fed from one ticket queue (the persistent grid's setting):
-    makespan, per-unit spans, busy and waiting time, deadlock detection.
+    makespan, per-unit spans, busy and waiting time, deadlock detection;
+    ticket orders one head after another or in interleaved runs of heads.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things the
 oracle does not compute itself: finite differences, closed forms, invariants,

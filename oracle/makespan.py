@@ -47,6 +47,20 @@ def ticket_order(plan: Sch.Plan, heads: int, worker_order=None):
     return [(h, w) for h in range(heads) for w in order]
 
 
+def interleaved_ticket_order(plan: Sch.Plan, heads: int, ilv: int):
+    """Tickets [(head, worker)] dealt in runs of `ilv` heads, worker by
+    worker: worker 0 of each head of the run, then worker 1 of each, and so
+    on; a last run may hold fewer heads. ilv = 1 is ticket_order(plan, heads)."""
+    if ilv < 1:
+        raise ValueError("ilv must be at least 1")
+    n = len(plan.workers)
+    out = []
+    for first in range(0, heads, ilv):
+        run = range(first, min(heads, first + ilv))
+        out += [(h, w) for w in range(n) for h in run]
+    return out
+
+
 def simulate(plan: Sch.Plan, heads: int, processors: int, c: float = 1.0, r: float = 0.0,
              tickets=None):
     """Run every unit of `heads` copies of `plan` on `processors` processors.
