@@ -1,6 +1,6 @@
 """torch.autograd wrapper and a synthetic attention block over the library.
 
-    out = attention(q, k, v, causal=True, schedule="shift")   # differentiable
+    out = attention(q, k, v, causal=True, schedule="descending")   # differentiable
     block = AttentionBlock(hidden=4096, heads=32, kv_heads=8, head_dim=128)
 
 The forward runs the library's attention forward (O and the log-sum-exp it
@@ -47,8 +47,12 @@ class _Attention(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
 
-def attention(q, k, v, causal: bool = True, schedule="shift", scale: float | None = None):
-    """Differentiable softmax attention; schedule=None uses the atomic-dQ backward."""
+def attention(q, k, v, causal: bool = True, schedule="descending", scale: float | None = None):
+    """Differentiable softmax attention; schedule=None uses the atomic-dQ backward.
+
+    The default, Descending, measured fastest on the causal shapes timed (4k
+    and 8k, also with grouped K/V heads) and on the 16k full mask, and 3-6%
+    behind Shift on the 2k and 4k full masks."""
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     return _Attention.apply(q, k, v, causal, schedule, float(scale))
@@ -67,7 +71,7 @@ def rotary(x, base: float = 500000.0):
 class AttentionBlock(torch.nn.Module):
     """x + Wo . attention(rope(Wq n(x)), rope(Wk n(x)), Wv n(x)), n = RMS norm; random bf16 weights."""
 
-    def __init__(self, hidden=4096, heads=32, kv_heads=8, head_dim=128, causal=True, schedule="shift", seed=0,
+    def __init__(self, hidden=4096, heads=32, kv_heads=8, head_dim=128, causal=True, schedule="descending", seed=0,
                  device="cuda"):
         super().__init__()
         g = torch.Generator(device="cpu").manual_seed(seed)
