@@ -89,7 +89,7 @@ def tile(S: int, D: int, tile_request: int = 0) -> int:
     return t
 
 
-def workspace_size(B, H, S, D, causal, schedule="naive", tile_request=0, Hkv=None) -> int:
+def workspace_size(B, H, S, D, causal, schedule="descending", tile_request=0, Hkv=None) -> int:
     """Workspace bytes; Hkv = number of K/V heads when query heads share them (default H)."""
     mask = MASK_CAUSAL if causal else MASK_FULL
     if Hkv is None or int(Hkv) == int(H):
@@ -103,7 +103,7 @@ def workspace_size(B, H, S, D, causal, schedule="naive", tile_request=0, Hkv=Non
     return int(n)
 
 
-def alloc_workspace(B, H, S, D, causal, schedule="naive", tile_request=0, device="cuda", Hkv=None):
+def alloc_workspace(B, H, S, D, causal, schedule="descending", tile_request=0, device="cuda", Hkv=None):
     """Device workspace (uint8) for bwd/bwd_nondeterministic with these arguments."""
     torch = _torch()
     return torch.empty(workspace_size(B, H, S, D, causal, schedule, tile_request, Hkv), dtype=torch.uint8,
@@ -131,7 +131,7 @@ def fwd(q, k, v, causal: bool, scale: float | None = None, out=None):
     return o, lse
 
 
-def bwd(q, k, v, o, do, lse, causal: bool, schedule="naive", scale: float | None = None, tile_request: int = 0,
+def bwd(q, k, v, o, do, lse, causal: bool, schedule="descending", scale: float | None = None, tile_request: int = 0,
         workspace=None, out=None):
     """Deterministic attention backward; returns (dq, dk, dv) bf16 shaped like (q, k, v)."""
     return _bwd(q, k, v, o, do, lse, causal, _sched(schedule), scale, tile_request, workspace, out, True)
@@ -180,7 +180,7 @@ def _bwd(q, k, v, o, do, lse, causal, schedule, scale, tile_request, workspace, 
     return dq, dk, dv
 
 
-def bwd_noalloc(q, k, v, o, do, lse, causal: bool, schedule="naive", scale: float | None = None,
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool, schedule="descending", scale: float | None = None,
                 tile_request: int = 0, out=None):
     """attn_bwd_deterministic_noalloc: the deterministic backward with the library's static
     scratch as its workspace (no device allocation in the call when `out` is given); plain
